@@ -1,0 +1,207 @@
+"""Python binding of libmoe_nvfp4.so: one NVFP4 sparse-MoE FFN layer on MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.  torch is
+used for device memory and streams.  The functions mirror the C ABI in include/moe_nvfp4.h
+(same names without the `moe_` prefix); they check dtype, device, shape and contiguity, raise
+ValueError on bad arguments and RuntimeError with the library's status text on a failing call.
+There is no fallback: if the library is missing, loading it raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
+
+MOE_F32 = 0
+MOE_F16 = 1
+_lib = None
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p),
+                ("down_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
+                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("E", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+
+def lib():
+    """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe_nvfp4.so not found at %s: build it first "
+                               "(python -m bit_expert_ffn_amd.build)" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.moe_abi_version.restype = i32
+        L.moe_abi_version.argtypes = []
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [i32]
+        L.moe_workspace_size.restype = sz
+        L.moe_workspace_size.argtypes = [i32] * 5
+        L.moe_route.restype = i32
+        L.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_group.restype = i32
+        L.moe_group.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn_nvfp4.restype = i32
+        L.moe_expert_ffn_nvfp4.argtypes = [vp, ctypes.POINTER(_Experts), vp, vp, vp, vp, vp,
+                                           i32, i32, vp, i32, vp, sz, vp]
+        L.moe_combine.restype = i32
+        L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
+            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine")
+
+
+def abi_version():
+    return lib().moe_abi_version()
+
+
+def status_string(code):
+    return lib().moe_status_string(int(code)).decode()
+
+
+def workspace_size(T, H, I, E, k):
+    return int(lib().moe_workspace_size(T, H, I, E, k))
+
+
+def _check(code, what):
+    if code != 0:
+        raise RuntimeError("%s failed: %d (%s)" % (what, code, status_string(code)))
+
+
+def _dev(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def route(x, w_router, bias, k, topk_id, topk_w, ws, logits=None, stream=None):
+    """moe_route: x [T][H] bf16, w_router [H][E] fp32, bias [E] fp32 or None ->
+    topk_id [T][k] int32, topk_w [T][k] fp32 (and logits [T][E] fp32 if given)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    args = (_dev(x, "x", torch.bfloat16), _dev(w_router, "w_router", torch.float32, (H, E)),
+            None if bias is None else _dev(bias, "bias", torch.float32, (E,)), T, H, E, k,
+            None if logits is None else _dev(logits, "logits", torch.float32, (T, E)),
+            _dev(topk_id, "topk_id", torch.int32, (T, k)),
+            _dev(topk_w, "topk_w", torch.float32, (T, k)), _dev(ws, "ws", torch.uint8),
+            ws.numel(), _stream(stream, x.device))
+    _check(lib().moe_route(*args), "moe_route")
+
+
+def group(topk_id, E, count, offset, sorted_slot, slot_row, active, n_active, ws, stream=None):
+    """moe_group: stable grouping of the T*k slots by expert (outputs are int32 tensors)."""
+    T, k = topk_id.shape
+    n = T * k
+    args = (_dev(topk_id, "topk_id", torch.int32), T, k, E,
+            _dev(count, "count", torch.int32, (E,)), _dev(offset, "offset", torch.int32, (E + 1,)),
+            _dev(sorted_slot, "sorted_slot", torch.int32, (n,)),
+            _dev(slot_row, "slot_row", torch.int32, (n,)),
+            _dev(active, "active", torch.int32, (E,)),
+            _dev(n_active, "n_active", torch.int32, (1,)), _dev(ws, "ws", torch.uint8),
+            ws.numel(), _stream(stream, topk_id.device))
+    _check(lib().moe_group(*args), "moe_group")
+
+
+def experts_struct(experts):
+    """ctypes struct for a dict of NVFP4 expert tensors (gate_q, up_q, down_q, gate_s, up_s,
+    down_s: uint8; ts: [E][3] float32)."""
+    E, I, h2 = experts["gate_q"].shape
+    H = h2 * 2
+    shapes = dict(gate_q=(E, I, H // 2), up_q=(E, I, H // 2), down_q=(E, H, I // 2),
+                  gate_s=(E, I, H // 16), up_s=(E, I, H // 16), down_s=(E, H, I // 16))
+    ptr = {n: _dev(experts[n], n, torch.uint8, s) for n, s in shapes.items()}
+    ts = _dev(experts["ts"], "ts", torch.float32, (E, 3))
+    return _Experts(ptr["gate_q"], ptr["up_q"], ptr["down_q"], ptr["gate_s"], ptr["up_s"],
+                    ptr["down_s"], ts, E, H, I)
+
+
+def expert_ffn_nvfp4(x, experts, count, offset, sorted_slot, active, n_active, k, y, ws,
+                     stream=None):
+    """moe_expert_ffn_nvfp4: y [T*k][H] (float32 or float16) in grouped row order."""
+    T, H = x.shape
+    s = experts_struct(experts)
+    if s.H != H:
+        raise ValueError("x hidden size %d does not match experts %d" % (H, s.H))
+    if y.dtype == torch.float32:
+        yd = MOE_F32
+    elif y.dtype == torch.float16:
+        yd = MOE_F16
+    else:
+        raise ValueError("y must be float32 or float16")
+    E = s.E
+    args = (_dev(x, "x", torch.bfloat16), ctypes.byref(s), _dev(count, "count", torch.int32, (E,)),
+            _dev(offset, "offset", torch.int32, (E + 1,)),
+            _dev(sorted_slot, "sorted_slot", torch.int32, (T * k,)),
+            _dev(active, "active", torch.int32, (E,)),
+            _dev(n_active, "n_active", torch.int32, (1,)), T, k,
+            _dev(y, "y", y.dtype, (T * k, H)), yd, _dev(ws, "ws", torch.uint8), ws.numel(),
+            _stream(stream, x.device))
+    _check(lib().moe_expert_ffn_nvfp4(*args), "moe_expert_ffn_nvfp4")
+
+
+def combine(y, slot_row, topk_w, out, stream=None):
+    """moe_combine: out [T][H] fp32 = routing-weighted sum of each token's k expert rows."""
+    T, k = topk_w.shape
+    H = y.shape[1]
+    yd = MOE_F16 if y.dtype == torch.float16 else MOE_F32
+    args = (_dev(y, "y", y.dtype, (T * k, H)), yd, _dev(slot_row, "slot_row", torch.int32, (T * k,)),
+            _dev(topk_w, "topk_w", torch.float32, (T, k)), T, k, H,
+            _dev(out, "out", torch.float32, (T, H)), _stream(stream, y.device))
+    _check(lib().moe_combine(*args), "moe_combine")
+
+
+class LayerBuffers:
+    """Device buffers for one layer call of given sizes (plain torch allocations)."""
+
+    def __init__(self, T, H, I, E, k, device="cuda", y_dtype=torch.float32, logits=True):
+        d = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=d)
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=d) if logits else None
+        self.topk_id = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.count = torch.empty(E, **i32)
+        self.offset = torch.empty(E + 1, **i32)
+        self.sorted_slot = torch.empty(T * k, **i32)
+        self.slot_row = torch.empty(T * k, **i32)
+        self.active = torch.empty(E, **i32)
+        self.n_active = torch.empty(1, **i32)
+        self.y = torch.empty((T * k, H), dtype=y_dtype, device=d)
+        self.out = torch.empty((T, H), dtype=torch.float32, device=d)
+        n = workspace_size(T, H, I, E, k)
+        if n == 0:
+            raise ValueError("unsupported layer shape T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
+        self.ws = torch.empty(n, dtype=torch.uint8, device=d)
+
+
+def layer(x, w_router, bias, experts, k, buf, stream=None):
+    """The four calls in order; results are left in `buf` (out, topk ids/weights, grouping, y)."""
+    route(x, w_router, bias, k, buf.topk_id, buf.topk_w, buf.ws, logits=buf.logits, stream=stream)
+    group(buf.topk_id, w_router.shape[1], buf.count, buf.offset, buf.sorted_slot, buf.slot_row,
+          buf.active, buf.n_active, buf.ws, stream=stream)
+    expert_ffn_nvfp4(x, experts, buf.count, buf.offset, buf.sorted_slot, buf.active,
+                     buf.n_active, k, buf.y, buf.ws, stream=stream)
+    combine(buf.y, buf.slot_row, buf.topk_w, buf.out, stream=stream)
+    return buf.out

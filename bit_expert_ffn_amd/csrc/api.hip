@@ -1,0 +1,165 @@
+// C ABI of libmoe_nvfp4.so (declarations and contracts in include/moe_nvfp4.h).
+// Every entry point validates its arguments on the host before enqueueing anything; a failing
+// check returns an error code and launches nothing.
+#include "../../include/moe_nvfp4.h"
+
+#include "common.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+WsLayout ws_layout(int T, int H, int I, int E, int k) {
+  WsLayout L;
+  const RoutePlan p = route_plan(T, H, E);
+  L.route_partial = 0;
+  L.route_end = align_up((size_t)p.KS * T * E * sizeof(float), 256);
+  const size_t n = (size_t)T * k;
+  L.group_whist = 0;
+  L.group_end = 0;
+  if (n > (size_t)kGroupSmallMax) {
+    const size_t nblk = (n + kGroupChunk - 1) / kGroupChunk;
+    L.group_end = align_up(nblk * 16 * E * sizeof(int32_t), 256);
+  }
+  L.ffn_x16 = 0;
+  L.ffn_h16 = align_up((size_t)T * H * sizeof(_Float16), 256);
+  L.ffn_end = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
+  size_t tot = L.route_end;
+  if (L.group_end > tot) tot = L.group_end;
+  if (L.ffn_end > tot) tot = L.ffn_end;
+  L.total = tot;
+  return L;
+}
+
+}  // namespace moe
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  if (T < 1 || k < 1 || E < 1 || k > E || H < 1 || I < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (H % 128 != 0 || I % 128 != 0 || H > 65536 || I > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T * k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+MOE_API int32_t moe_abi_version(void) { return MOE_NVFP4_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument (NULL or misaligned pointer, bad size or dtype)";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (E > 256, H or I not a multiple of 128 or above 65536, or T*k >= 2^31)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
+  if (check_shape(T, H, I, E, k) != MOE_OK) return 0;
+  return moe::ws_layout(T, H, I, E, k).total;
+}
+
+MOE_API moe_status moe_route(const void* x_dev, const float* w_router_dev, const float* bias_dev,
+                             int32_t T, int32_t H, int32_t E, int32_t k, float* logits_dev,
+                             int32_t* topk_id_dev, float* topk_w_dev, void* ws_dev,
+                             size_t ws_bytes, void* stream) {
+  if (!x_dev || !w_router_dev || !topk_id_dev || !topk_w_dev || !ws_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x_dev) || !aligned16(w_router_dev) || !aligned16(topk_id_dev) ||
+      !aligned16(topk_w_dev) || !aligned16(ws_dev) || (bias_dev && !aligned16(bias_dev)) ||
+      (logits_dev && !aligned16(logits_dev)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  // the router does not depend on I: validate with the smallest legal I
+  moe_status st = check_shape(T, H, 128, E, k);
+  if (st != MOE_OK) return st;
+  const moe::WsLayout L = moe::ws_layout(T, H, 128, E, k);
+  if (ws_bytes < L.route_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  float* partial = reinterpret_cast<float*>((char*)ws_dev + L.route_partial);
+  return from_hip(moe::launch_route((const uint16_t*)x_dev, w_router_dev, bias_dev, T, H, E, k,
+                                    logits_dev, topk_id_dev, topk_w_dev, partial,
+                                    (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_group(const int32_t* topk_id_dev, int32_t T, int32_t k, int32_t E,
+                             int32_t* count_dev, int32_t* offset_dev, int32_t* sorted_slot_dev,
+                             int32_t* slot_row_dev, int32_t* active_dev, int32_t* n_active_dev,
+                             void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!topk_id_dev || !count_dev || !offset_dev || !sorted_slot_dev || !slot_row_dev ||
+      !active_dev || !n_active_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(topk_id_dev) || !aligned16(count_dev) || !aligned16(offset_dev) ||
+      !aligned16(sorted_slot_dev) || !aligned16(slot_row_dev) || !aligned16(active_dev) ||
+      !aligned16(n_active_dev))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, 128, 128, E, k);
+  if (st != MOE_OK) return st;
+  const moe::WsLayout L = moe::ws_layout(T, 128, 128, E, k);
+  if (L.group_end > 0) {
+    if (!ws_dev || !aligned16(ws_dev)) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < L.group_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  int32_t* whist = reinterpret_cast<int32_t*>((char*)ws_dev + L.group_whist);
+  return from_hip(moe::launch_group(topk_id_dev, T, k, E, count_dev, offset_dev,
+                                    sorted_slot_dev, slot_row_dev, active_dev, n_active_dev,
+                                    whist, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_experts* w,
+                                        const int32_t* count_dev, const int32_t* offset_dev,
+                                        const int32_t* sorted_slot_dev, const int32_t* active_dev,
+                                        const int32_t* n_active_dev, int32_t T, int32_t k,
+                                        void* y_dev, int32_t y_dtype, void* ws_dev,
+                                        size_t ws_bytes, void* stream) {
+  if (!x_dev || !w || !count_dev || !offset_dev || !sorted_slot_dev || !active_dev ||
+      !n_active_dev || !y_dev || !ws_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->gate_q || !w->up_q || !w->down_q || !w->gate_s || !w->up_s || !w->down_s ||
+      !w->tensor_scale)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_F16) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x_dev, count_dev, offset_dev, sorted_slot_dev, active_dev, n_active_dev,
+                        y_dev, ws_dev, w->gate_q, w->up_q, w->down_q, w->gate_s, w->up_s,
+                        w->down_s, w->tensor_scale};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st != MOE_OK) return st;
+  const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
+  if (ws_bytes < L.ffn_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  moe::FfnArgs a;
+  a.x = (const uint16_t*)x_dev;
+  a.gq = w->gate_q; a.uq = w->up_q; a.dq = w->down_q;
+  a.gs = w->gate_s; a.us = w->up_s; a.ds = w->down_s;
+  a.ts = w->tensor_scale;
+  a.count = count_dev; a.offset = offset_dev; a.sorted_slot = sorted_slot_dev;
+  a.active = active_dev; a.n_active = n_active_dev;
+  a.T = T; a.k = k; a.E = w->E; a.H = w->H; a.I = w->I;
+  a.y = y_dev;
+  a.y_f16 = y_dtype == MOE_F16;
+  a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
+  a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
+  return from_hip(moe::launch_ffn(a, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t* slot_row_dev,
+                               const float* topk_w_dev, int32_t T, int32_t k, int32_t H,
+                               float* out_dev, void* stream) {
+  if (!y_dev || !slot_row_dev || !topk_w_dev || !out_dev) return MOE_ERR_INVALID_ARGUMENT;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_F16) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_dev) || !aligned16(slot_row_dev) || !aligned16(topk_w_dev) ||
+      !aligned16(out_dev))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, H, 128, k, k);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_combine(y_dev, y_dtype == MOE_F16, slot_row_dev, topk_w_dev, T, k,
+                                      H, out_dev, (hipStream_t)stream));
+}

@@ -1,0 +1,67 @@
+// Internal declarations shared by the HIP sources of libmoe_nvfp4 (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+namespace moe {
+
+constexpr int kMaxExperts = 256;
+// rows handled by the one-block grouping kernel; above this the three-pass grouping runs
+constexpr int kGroupSmallMax = 16384;
+// slots per block of the three-pass grouping (16 waves x 1024 slots)
+constexpr int kGroupChunk = 16384;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Router launch plan: TT tokens per block, the hidden dimension split into KS slices of kc.
+struct RoutePlan {
+  int TT, KS, kc;
+};
+RoutePlan route_plan(int T, int H, int E);
+
+// Byte offsets of every call's scratch inside the caller's workspace.
+struct WsLayout {
+  size_t route_partial;  // [KS][T][E] fp32
+  size_t route_end;
+  size_t group_whist;    // [nblk*16][E] int32 (three-pass grouping only)
+  size_t group_end;
+  size_t ffn_x16;        // [T][H] f16
+  size_t ffn_h16;        // [T*k][I] f16
+  size_t ffn_end;
+  size_t total;
+};
+WsLayout ws_layout(int T, int H, int I, int E, int k);
+
+hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H,
+                        int E, int k, float* logits, int32_t* topk_id, float* topk_w,
+                        float* partial, hipStream_t s);
+hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* count,
+                        int32_t* offset, int32_t* sorted_slot, int32_t* slot_row,
+                        int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s);
+
+struct FfnArgs {
+  const uint16_t* x;  // [T][H] bf16
+  const uint8_t *gq, *uq, *dq, *gs, *us, *ds;
+  const float* ts;
+  const int32_t *count, *offset, *sorted_slot, *active, *n_active;
+  int T, k, E, H, I;
+  void* y;
+  int y_f16;
+  _Float16* x16;  // workspace
+  _Float16* h16;  // workspace
+};
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const void* y, int y_f16, const int32_t* slot_row, const float* w,
+                          int T, int k, int H, float* out, hipStream_t s);
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+}  // namespace moe

@@ -1,0 +1,150 @@
+/*
+ * moe_nvfp4.h -- C ABI of libmoe_nvfp4.so: one sparse mixture-of-experts FFN layer with NVFP4
+ * (4-bit) expert weights on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the source pages state it:
+ *   - a router sends every token to k of E experts (8 of 256 in the pages' model):
+ *     "Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", Background / "The model";
+ *   - expert weights are 4-bit with one scale per 16 values, a microscaling format: same page,
+ *     "NVFP4 experts"; weights stay 4-bit until they are unpacked in registers, never
+ *     dequantised to HBM: "Optimizing Models to Be Fast at Codegen", section 2 "Kernels
+ *     optimized for latency or throughput";
+ *   - each chosen expert runs gate/up, SwiGLU and down, and the token's owner adds the expert
+ *     outputs in a weighted sum: "Optimizing Muse Spark Open ...", section 8 "Prefill: a fused
+ *     MoE kernel and fair batching" ("The fused MoE kernel and the pair exchange", "A one-pass
+ *     combine");
+ *   - busy and few-row experts take different paths after a step's experts are sorted by row
+ *     count: same page, section 5 "Keeping register pressure off the common path";
+ *   - index building stays on the device, with no host synchronisation: "Day-0 Inference
+ *     Adaptation for Ultra-Large Sparse Models", "Operator Layer", Index Pipeline.
+ * Readings taken where the pages are silent: the block scale is OCP E4M3FN, every expert matrix
+ * also has one fp32 tensor scale, and the routing weights are the softmax over the k selected
+ * logits (equal to the full softmax renormalised over them).
+ *
+ * Four calls make one layer, in this order on one stream:
+ *     moe_route -> moe_group -> moe_expert_ffn_nvfp4 -> moe_combine
+ *
+ * Conventions for every call
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA tensors); everything
+ *     else is host memory read during the call.  Device pointers must be 16-byte aligned.
+ *     Arrays are dense, row-major, with the last index contiguous.
+ *   - Ownership: the caller allocates and frees every buffer.  The library never allocates,
+ *     frees or keeps a pointer after a call returns; kernels still queued on `stream` read and
+ *     write the buffers until they finish.  The library holds no state and calls may come from
+ *     any thread; calls that share a workspace must be ordered on one stream.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is asynchronous: it
+ *     validates its arguments on the host, enqueues kernels on `stream` and returns.  There is
+ *     no host-device synchronisation inside any call.
+ *   - Errors: arguments are checked before anything is enqueued; a failing check returns a
+ *     negative moe_status and launches nothing.  A launch failure returns MOE_ERR_HIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation.  Expert ids are trusted
+ *     (they come from moe_route); ids outside [0, E) are undefined behaviour.  NaN/Inf inputs
+ *     propagate; there are no device-side checks.
+ *   - Shape limits: 1 <= k <= E <= 256; H and I multiples of 128 with 128 <= H, I <= 65536;
+ *     T >= 1 and T*k < 2^31.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_NVFP4_ABI_VERSION 1
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1,   /* NULL pointer, misaligned pointer, T < 1, k > E, bad dtype */
+  MOE_ERR_UNSUPPORTED_SHAPE = -2,  /* H or I not a multiple of 128, E > 256, sizes too large   */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_HIP = -4,                /* a HIP launch or runtime call failed                      */
+  MOE_ERR_INTERNAL = -5
+};
+
+/* element type tag of the expert-output buffer y */
+enum { MOE_F32 = 0, MOE_F16 = 1 };
+
+/* NVFP4 expert weights.  All pointers are device pointers.  For every expert e:
+ *   gate_q, up_q [E][I][H/2]  e2m1 codes, two per byte, low nibble = even k (k runs over H)
+ *   gate_s, up_s [E][I][H/16] e4m3 (OCP E4M3FN) scale codes, one per 16 consecutive k of a row
+ *   down_q       [E][H][I/2]  e2m1 codes, k runs over I
+ *   down_s       [E][H][I/16] e4m3 scale codes
+ *   tensor_scale [E][3]       fp32 scales of gate, up and down
+ * Weight value: W[n][k] = e2m1(code) * e4m3(scale of block k/16) * tensor_scale.
+ * The struct itself is host memory, read during the call only. */
+typedef struct moe_nvfp4_experts {
+  const uint8_t *gate_q, *up_q, *down_q;
+  const uint8_t *gate_s, *up_s, *down_s;
+  const float *tensor_scale;
+  int32_t E, H, I;
+} moe_nvfp4_experts;
+
+/* Version of this ABI (MOE_NVFP4_ABI_VERSION of the built library). */
+int32_t moe_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char *moe_status_string(moe_status status);
+
+/* Bytes of device workspace that every call of a layer with these sizes needs (one buffer
+ * serves all four calls).  Returns 0 if the sizes are outside the shape limits. */
+size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
+
+/* Router and top-k ("The model": every token is routed to k of E experts).
+ *   x_dev        [T][H] bf16 activations
+ *   w_router_dev [H][E] fp32 router weights
+ *   bias_dev     [E] fp32 added to every token's logits, or NULL
+ *   logits_dev   [T][E] fp32 output, or NULL: logits[t][e] = sum_h x[t][h] * Wr[h][e] + bias[e],
+ *                accumulated in fp32
+ *   topk_id_dev  [T][k] int32 output: the k largest logits of each token in descending order,
+ *                equal logits by ascending expert id
+ *   topk_w_dev   [T][k] fp32 output: exp(l_j - l_max) / sum over the selected of exp(l - l_max)
+ *   ws_dev       workspace of ws_bytes >= moe_workspace_size(...) bytes (contents scratch) */
+moe_status moe_route(const void *x_dev, const float *w_router_dev, const float *bias_dev,
+                     int32_t T, int32_t H, int32_t E, int32_t k, float *logits_dev,
+                     int32_t *topk_id_dev, float *topk_w_dev, void *ws_dev, size_t ws_bytes,
+                     void *stream);
+
+/* Token-to-expert grouping: a stable counting sort of the T*k (token, slot) pairs by expert,
+ * built on the device (Day-0 page, Index Pipeline), plus the experts sorted by row count for
+ * the few-row / busy split (Muse Spark page, section 5).  Outputs (device, int32):
+ *   count_dev       [E]    rows routed to each expert
+ *   offset_dev      [E+1]  exclusive prefix sum of count; offset[E] = T*k
+ *   sorted_slot_dev [T*k]  slot t*k+j of each row, rows ordered by (expert, t, j)
+ *   slot_row_dev    [T*k]  inverse: the row that slot t*k+j landed on
+ *   active_dev      [E]    experts with count > 0 by count descending then id ascending; the
+ *                          remaining entries are -1
+ *   n_active_dev    [1]    number of experts with count > 0
+ * Every output is bit-exact and deterministic. */
+moe_status moe_group(const int32_t *topk_id_dev, int32_t T, int32_t k, int32_t E,
+                     int32_t *count_dev, int32_t *offset_dev, int32_t *sorted_slot_dev,
+                     int32_t *slot_row_dev, int32_t *active_dev, int32_t *n_active_dev,
+                     void *ws_dev, size_t ws_bytes, void *stream);
+
+/* Expert FFN for every routed row (Muse Spark page, section 8: gate/up, SwiGLU, down):
+ *   g = Wg.x, u = Wu.x, h = g / (1 + exp(-g)) * u, y = Wd.h
+ * x_dev is [T][H] bf16; the grouping arrays are moe_group's outputs for the same T, k and E.
+ * y_dev is [T*k][H] in grouped row order (row r belongs to sorted_slot[r]), of element type
+ * y_dtype (MOE_F32 or MOE_F16).  Packed weights are decoded in registers and never written
+ * out.  Arithmetic: x and h enter the matrix cores as f16, the decoded weights
+ * e2m1 * e4m3 are exact in f16, products accumulate in fp32, h is stored as f16. */
+moe_status moe_expert_ffn_nvfp4(const void *x_dev, const moe_nvfp4_experts *w, const int32_t *count_dev,
+                                const int32_t *offset_dev, const int32_t *sorted_slot_dev,
+                                const int32_t *active_dev, const int32_t *n_active_dev, int32_t T,
+                                int32_t k, void *y_dev, int32_t y_dtype, void *ws_dev,
+                                size_t ws_bytes, void *stream);
+
+/* Routing-weighted combine (Muse Spark page, section 8, "A one-pass combine"; "No zero fill"):
+ *   out[t][n] = sum over j = 0..k-1 of topk_w[t][j] * y[slot_row[t*k+j]][n], in fp32.
+ * Reads y once and writes every out row exactly once.  out_dev is [T][H] fp32. */
+moe_status moe_combine(const void *y_dev, int32_t y_dtype, const int32_t *slot_row_dev,
+                       const float *topk_w_dev, int32_t T, int32_t k, int32_t H, float *out_dev,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

@@ -1,0 +1,134 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the header declares,
+and rejects bad arguments with the documented status before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_expert_ffn_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+OK, INVALID, SHAPE, WS = 0, -1, -2, -3
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced, every case fails first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    declared = _declared()
+    assert set(declared) == set(moe.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert moe.abi_version() == 1
+    for code in (OK, INVALID, SHAPE, WS, -4, -5, 7):
+        assert isinstance(moe.status_string(code), str) and moe.status_string(code)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,ok", [
+    (1, 7168, 2048, 256, 8, True), (4, 256, 128, 8, 2, True), (16384, 7168, 2048, 256, 8, True),
+    (0, 256, 128, 8, 2, False), (4, 250, 128, 8, 2, False), (4, 256, 100, 8, 2, False),
+    (4, 256, 128, 300, 2, False), (4, 256, 128, 8, 9, False), (4, 256, 128, 8, 0, False),
+])
+def test_workspace_size(T, H, I, E, k, ok):
+    n = moe.workspace_size(T, H, I, E, k)
+    assert (n > 0) == ok
+    if ok:
+        assert n % 256 == 0
+        # the FFN needs at least x and h in f16
+        assert n >= T * H * 2 + T * k * I * 2
+
+
+def _route(**over):
+    a = dict(x=A, wr=A, bias=None, T=4, H=256, E=8, k=2, logits=None, ids=A, w=A, ws=A,
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return moe.lib().moe_route(a["x"], a["wr"], a["bias"], a["T"], a["H"], a["E"], a["k"],
+                               a["logits"], a["ids"], a["w"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_route_rejects_bad_arguments():
+    assert _route(x=None) == INVALID
+    assert _route(ids=None) == INVALID
+    assert _route(x=A + 2) == INVALID
+    assert _route(bias=A + 4) == INVALID
+    assert _route(T=0) == INVALID
+    assert _route(k=9) == INVALID
+    assert _route(k=0) == INVALID
+    assert _route(E=300, k=2) == SHAPE
+    assert _route(H=200) == SHAPE
+    assert _route(ws_bytes=16) == WS
+
+
+def _group(**over):
+    a = dict(ids=A, T=4, k=2, E=8, ws=A, ws_bytes=1 << 30)
+    a.update(over)
+    return moe.lib().moe_group(a["ids"], a["T"], a["k"], a["E"], A, A, A, A, A, A, a["ws"],
+                               a["ws_bytes"], None)
+
+
+def test_group_rejects_bad_arguments():
+    assert _group(ids=None) == INVALID
+    assert _group(ids=A + 8) == INVALID
+    assert _group(T=0) == INVALID
+    assert _group(E=257, k=2) == SHAPE
+    assert _group(k=9) == INVALID
+    # the three-pass grouping needs workspace
+    assert _group(T=4096, k=8, E=256, ws_bytes=0) == WS
+    assert _group(T=4096, k=8, E=256, ws=None) == INVALID
+
+
+def _experts(**over):
+    f = dict(gate_q=A, up_q=A, down_q=A, gate_s=A, up_s=A, down_s=A, tensor_scale=A, E=8, H=256, I=128)
+    f.update(over)
+    return moe._Experts(**f)
+
+
+def _ffn(w=None, **over):
+    a = dict(x=A, T=4, k=2, y=A, yd=0, ws=A, ws_bytes=1 << 30)
+    a.update(over)
+    s = w if w is not None else _experts()
+    return moe.lib().moe_expert_ffn_nvfp4(a["x"], ctypes.byref(s), A, A, A, A, A, a["T"], a["k"],
+                                          a["y"], a["yd"], a["ws"], a["ws_bytes"], None)
+
+
+def test_ffn_rejects_bad_arguments():
+    assert _ffn(x=None) == INVALID
+    assert _ffn(yd=2) == INVALID
+    assert _ffn(y=A + 1) == INVALID
+    assert _ffn(_experts(down_s=None)) == INVALID
+    assert _ffn(_experts(gate_q=A + 4)) == INVALID
+    assert _ffn(_experts(H=200)) == SHAPE
+    assert _ffn(_experts(I=96)) == SHAPE
+    assert _ffn(_experts(E=512)) == SHAPE
+    assert _ffn(k=9) == INVALID
+    assert _ffn(T=0) == INVALID
+    assert _ffn(ws_bytes=1024) == WS
+    assert moe.lib().moe_expert_ffn_nvfp4(A, None, A, A, A, A, A, 4, 2, A, 0, A, 1 << 30, None) == INVALID
+
+
+def test_combine_rejects_bad_arguments():
+    c = moe.lib().moe_combine
+    assert c(None, 0, A, A, 4, 2, 256, A, None) == INVALID
+    assert c(A, 3, A, A, 4, 2, 256, A, None) == INVALID
+    assert c(A, 0, A, A + 4, 4, 2, 256, A, None) == INVALID
+    assert c(A, 0, A, A, 0, 2, 256, A, None) == INVALID
+    assert c(A, 0, A, A, 4, 2, 200, A, None) == SHAPE
+
+
+def test_python_binding_validates_before_calling():
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.route(x, torch.zeros(256, 8), None, 2, torch.zeros(4, 2, dtype=torch.int32),
+                  torch.zeros(4, 2), torch.zeros(16, dtype=torch.uint8))

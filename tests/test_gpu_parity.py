@@ -1,0 +1,161 @@
+"""GPU parity of the HIP layer against the CPU oracle on seeded inputs that the oracle finishes
+in seconds: the tiny workload, shapes spanning several tiles with ragged tails, edge cases, and
+stage-by-stage checks on oracle-made inputs.  All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (check_out, check_routing, experts_np, gpu_layer, np_buf, oracle_token_out,
+                    LOGIT_TOL, out_errors)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny": dict(synth.SPECS["tiny"]),
+    "ragged_a": dict(T=37, H=512, I=256, E=16, k=4, router="normal", zipf=None),
+    "multi_tile": dict(T=200, H=256, I=384, E=32, k=6, router="normal", zipf=None),
+    "wide_k": dict(T=5, H=1024, I=128, E=64, k=8, router="normal", zipf=None),
+    "max_e": dict(T=64, H=256, I=128, E=256, k=8, router="uniform", zipf=None),
+    "single_expert": dict(T=33, H=256, I=256, E=1, k=1, router="normal", zipf=None),
+    "dense_k_eq_e": dict(T=6, H=256, I=128, E=8, k=8, router="normal", zipf=None),
+    "zipf_skew": dict(T=96, H=256, I=256, E=64, k=8, router="normal", zipf=1.1),
+}
+
+
+def _full_check(L, k, y_dtype=torch.float32):
+    print("case", L["spec"], "y", y_dtype, flush=True)
+    N = synth.to_numpy(L)
+    ex = experts_np(L["experts"])
+    ref = oracle.layer(N["x"], N["w_router"], N["bias"], ex, k)
+    g = np_buf(gpu_layer(L, k, y_dtype))
+    assert np.max(np.abs(g["logits"] - ref["logits"])) <= LOGIT_TOL
+    exempt = check_routing(g["topk_id"], g["topk_w"], ref["logits"], ref["topk_w"], k)
+    r_out = ref["out"].copy()
+    if not exempt:
+        for name in ("count", "offset", "sorted_slot", "slot_row", "active"):
+            assert np.array_equal(g[name], ref["group"][name]), name
+        assert int(g["n_active"][0]) == ref["group"]["n_active"]
+        check_out(g["y"], ref["y"])
+    for t, ids in exempt.items():
+        r_out[t] = oracle_token_out(N["x"], ex, t, ids, ref["logits"][t])
+    return check_out(g["out"], r_out)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_layer_parity(name):
+    L = synth.make_layer(SHAPES[name], seed=0)
+    _full_check(L, SHAPES[name]["k"])
+
+
+def test_layer_parity_f16_y():
+    L = synth.make_layer(SHAPES["ragged_a"], seed=1)
+    _full_check(L, SHAPES["ragged_a"]["k"], torch.float16)
+
+
+def test_all_rows_to_one_expert():
+    sp = dict(T=70, H=256, I=128, E=16, k=2, router="normal", zipf=None)
+    L = synth.make_layer(sp, seed=2)
+    bias = torch.zeros(16)
+    bias[3] = 100.0  # expert 3 is every token's first choice
+    L["bias"] = bias
+    _full_check(L, 2)
+
+
+def test_random_code_bytes_cover_every_decode():
+    """Every e2m1 code and every finite e4m3 scale code, positive and negative."""
+    sp = dict(T=8, H=256, I=128, E=4, k=2, router="normal", zipf=None)
+    L = synth.make_layer(sp, seed=3)
+    g = torch.Generator().manual_seed(3)
+    for n, t in L["experts"].items():
+        if n.endswith("_q"):
+            t.copy_(torch.randint(0, 256, t.shape, generator=g, dtype=torch.int32).to(torch.uint8))
+        elif n.endswith("_s"):
+            c = torch.randint(0, 254, t.shape, generator=g, dtype=torch.int32)
+            c = torch.where(c >= 127, c + 1, c)  # skip 0x7F and 0xFF (NaN)
+            t.copy_(c.to(torch.uint8))
+    L["experts"]["ts"].fill_(1.5e-4)
+    seen = set(L["experts"]["gate_s"].flatten().tolist())
+    assert seen == set(range(256)) - {0x7F, 0xFF}
+    _full_check(L, 2)
+
+
+def test_deterministic_bitwise():
+    L = synth.make_layer(SHAPES["multi_tile"], seed=4)
+    a = np_buf(gpu_layer(L, 6))
+    b = np_buf(gpu_layer(L, 6))
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+# ---------------------------------------------------------------- stage-by-stage
+def _dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (64, 8, 256), (2048, 8, 256), (2049, 8, 256),
+                                   (4096, 8, 256), (16384, 8, 256), (50, 3, 5)])
+def test_group_stage_bit_exact(T, k, E):
+    """moe_group on seeded ids (one-block path up to 16384 slots, three-pass above)."""
+    import bit_expert_ffn_amd as moe
+    rng = np.random.default_rng(T + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ref = oracle.group(ids, E)
+    ws = torch.empty(max(256, moe.workspace_size(T, 128, 128, E, k)), dtype=torch.uint8, device="cuda")
+    out = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
+           (("count", E), ("offset", E + 1), ("sorted_slot", T * k), ("slot_row", T * k),
+            ("active", E), ("n_active", 1))}
+    moe.group(_dev_i32(ids), E, out["count"], out["offset"], out["sorted_slot"], out["slot_row"],
+              out["active"], out["n_active"], ws)
+    torch.cuda.synchronize()
+    for n in ("count", "offset", "sorted_slot", "slot_row", "active"):
+        assert np.array_equal(out[n].cpu().numpy(), ref[n]), n
+    assert int(out["n_active"].item()) == ref["n_active"]
+
+
+def test_ffn_and_combine_stages_on_oracle_inputs():
+    import bit_expert_ffn_amd as moe
+    sp = SHAPES["multi_tile"]
+    L = synth.make_layer(sp, seed=5)
+    N = synth.to_numpy(L)
+    ex = experts_np(L["experts"])
+    k = sp["k"]
+    ids, w = oracle.topk(oracle.router(N["x"], N["w_router"]), k)
+    grp = oracle.group(ids, sp["E"])
+    y_ref = oracle.ffn(N["x"], ex, grp, k)
+    x = L["x"].cuda()
+    exd = {n: v.cuda() for n, v in L["experts"].items()}
+    T, H = x.shape
+    ws = torch.empty(moe.workspace_size(T, H, sp["I"], sp["E"], k), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    moe.expert_ffn_nvfp4(x, exd, _dev_i32(grp["count"]), _dev_i32(grp["offset"]),
+                         _dev_i32(grp["sorted_slot"]), _dev_i32(grp["active"]),
+                         _dev_i32([grp["n_active"]]), k, y, ws)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), y_ref)
+    # combine alone, on the oracle's y rounded to fp32 and its fp32 weights
+    y32 = torch.from_numpy(y_ref.astype(np.float32)).cuda()
+    w32 = torch.from_numpy(w.astype(np.float32)).cuda()
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.combine(y32, _dev_i32(grp["slot_row"]), w32, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y_ref.astype(np.float32), grp["slot_row"], w.astype(np.float32), k, H)
+    mr, ma = out_errors(out.cpu().numpy(), ref)
+    assert mr < 1e-6 and ma < 1e-7
+
+
+def test_route_stage_zero_input_and_ties():
+    """x = 0: every logit equals the bias; equal logits go to the lower expert id and the
+    weights are exactly 1/k."""
+    import bit_expert_ffn_amd as moe
+    T, H, E, k = 3, 256, 64, 8
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    wr = torch.randn((H, E), device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.workspace_size(T, H, 128, E, k), dtype=torch.uint8, device="cuda")
+    moe.route(x, wr, None, k, ids, w, ws)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == [list(range(k))] * T
+    assert torch.all(w.cpu() == 1.0 / k)
