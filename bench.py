@@ -1,0 +1,185 @@
+"""Benchmark of one NVFP4 sparse-MoE FFN layer on one MI355X.
+
+A step is one pass of the whole layer (moe_route -> moe_group -> moe_expert_ffn_nvfp4 ->
+moe_combine) over one batch of seeded synthetic tokens whose inputs are already resident in
+HBM.  Prints one JSON line (the benchmark contract) with the layer throughput, the roofline of
+the expert-FFN call (the kernel work that streams the expert weights) measured with HIP events
+on the launch stream over the timed region, and the CPU oracle timed on a bounded sample.
+
+Workloads (hidden 7168, 256 experts, top-8, NVFP4 experts):
+  decode1     T=1, expert intermediate 2048; each step takes the next token of a seeded pool of
+              64 tokens, so consecutive steps read different experts (as decoding does) rather
+              than re-reading a set that fits the 256 MB Infinity Cache   [default]
+  decode64    T=64, uniform-random router weights
+  verify128   T=128 (8 requests x 16 draft positions), intermediate 256 (one 1/8 shard),
+              Zipf(1.1) expert-popularity bias on the logits
+  prefill16k  T=16384 (8 x 2048)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + achieved HBM GB/s (T=1,64) / MFMA util (T=16K)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16/bf16 matrix throughput
+POOL = 64
+
+
+def expert_bytes(H, I):
+    """packed e2m1 codes + e4m3 scales of gate, up and down of one expert"""
+    return 3 * (H * I // 2 + H * I // 16)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode1",
+                    choices=["decode1", "decode64", "verify128", "prefill16k"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle sample budget (0 disables the CPU baseline)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import bit_expert_ffn_amd as moe
+    import synth
+
+    wl = args.workload
+    sp = dict(synth.SPECS[wl])
+    T, H, I, E, k = sp["T"], sp["H"], sp["I"], sp["E"], sp["k"]
+    big = wl == "prefill16k"
+    steps = args.steps if args.steps is not None else (10 if big else 200)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 20)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    print("generating %s inputs on the GPU" % wl, file=sys.stderr, flush=True)
+    pool = POOL if T == 1 else 1
+    layer = synth.make_layer(sp, seed=0, device=dev, T=T * pool)
+    xs = layer["x"]
+    wr, bias = layer["w_router"], layer["bias"]
+    ex = moe.pack_experts(layer["experts"])  # tile-major copy (load-time conversion)
+    buf = moe.LayerBuffers(T, H, I, E, k, device=dev, y_dtype=torch.float32, logits=False)
+    torch.cuda.synchronize()
+
+    def x_of(i):
+        j = (i % pool) * T
+        return xs[j:j + T]
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        x = x_of(i)
+        moe.route(x, wr, bias, k, buf.topk_id, buf.topk_w, buf.ws, stream=stream)
+        moe.group(buf.topk_id, E, buf.count, buf.offset, buf.sorted_slot, buf.slot_row,
+                  buf.active, buf.n_active, buf.ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        moe.expert_ffn_nvfp4(x, ex, buf.count, buf.offset, buf.sorted_slot, buf.active,
+                             buf.n_active, k, buf.y, buf.ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.combine(buf.y, buf.slot_row, buf.topk_w, buf.out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("warmup done; timing %d steps" % steps, file=sys.stderr, flush=True)
+
+    # timed region: exactly `steps` layer calls, bracketed by device synchronisation
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    n_distinct = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    # distinct experts touched per step (re-run routing+grouping outside the timed region)
+    for i in range(min(steps, POOL if T == 1 else 1)):
+        x = x_of(warmup + i)
+        moe.route(x, wr, bias, k, buf.topk_id, buf.topk_w, buf.ws, stream=stream)
+        moe.group(buf.topk_id, E, buf.count, buf.offset, buf.sorted_slot, buf.slot_row,
+                  buf.active, buf.n_active, buf.ws, stream=stream)
+        n_distinct.append(int(buf.n_active.item()))
+    nd = sum(n_distinct) / len(n_distinct)
+
+    ms_step = elapsed * 1e3 / steps
+    tok_s = T * steps / elapsed
+    w_bytes = nd * expert_bytes(H, I)
+    ffn_bytes = w_bytes + T * H * 2 + T * k * H * 4          # weights + x + y
+    layer_bytes = ffn_bytes + H * E * 4 + T * H * 4          # + router weights + out
+    flops = 6.0 * T * k * H * I
+    if big:
+        achieved = flops / (ffn_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_F16_PEAK_TFS,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFS, 4), traffic=None)
+    else:
+        achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(layer, sp, pool, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl, "T": T, "H": H, "I": I, "E": E, "k": k,
+                   "weights": "nvfp4 (e2m1, e4m3 per 16, fp32 per matrix)",
+                   "token_pool": pool, "seed": 0, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "us_per_layer": round(ms_step * 1e3, 2),
+        "ffn_us": round(ffn_ms * 1e3, 2),
+        "distinct_experts": round(nd, 2),
+        "layer_hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "ffn_algorithmic_bytes": int(ffn_bytes),
+        "ffn_flops": flops,
+    }
+    print(json.dumps(res))
+
+
+def cpu_baseline(layer, sp, pool, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload: whole-layer output of
+    as many tokens as fit the time budget (at least one), tokens/s."""
+    import numpy as np
+    import oracle
+    print("copying inputs to the host for the CPU oracle", file=sys.stderr, flush=True)
+    ex = oracle.Experts(**{n: v.cpu().numpy() for n, v in layer["experts"].items()})
+    x = layer["x"].cpu().view(torch.int16).numpy().view(np.uint16)
+    wr = layer["w_router"].cpu().numpy()
+    bias = None if layer["bias"] is None else layer["bias"].cpu().numpy()
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer_tokens(x, wr, bias, ex, sp["k"], [done % x.shape[0]])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s or done >= x.shape[0]:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 4), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d token(s) of the %s workload, whole layer per token (fp64 oracle)"
+                      % (done, "decode" if pool > 1 else "same")}
+
+
+if __name__ == "__main__":
+    main()

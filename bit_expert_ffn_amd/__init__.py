@@ -51,12 +51,14 @@ def lib():
                                            i32, i32, vp, i32, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_nvfp4_pack.restype = i32
+        L.moe_nvfp4_pack.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
-            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine")
+            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_nvfp4_pack")
 
 
 def abi_version():
@@ -68,6 +70,7 @@ def status_string(code):
 
 
 def workspace_size(T, H, I, E, k):
+    """Bytes of scratch workspace one layer call of these sizes needs."""
     return int(lib().moe_workspace_size(T, H, I, E, k))
 
 
@@ -124,9 +127,35 @@ def group(topk_id, E, count, offset, sorted_slot, slot_row, active, n_active, ws
     _check(lib().moe_group(*args), "moe_group")
 
 
+def nvfp4_pack(q, s, q_out=None, s_out=None, stream=None):
+    """moe_nvfp4_pack: row-major codes q [E][N][K/2] and scales s [E][N][K/16] (uint8, on the
+    GPU) -> tile-major tensors of the same shapes (new tensors unless given)."""
+    E, N, k2 = q.shape
+    K = k2 * 2
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if s_out is None:
+        s_out = torch.empty_like(s)
+    args = (_dev(q, "q", torch.uint8, (E, N, K // 2)), _dev(s, "s", torch.uint8, (E, N, K // 16)),
+            E, N, K, _dev(q_out, "q_out", torch.uint8, (E, N, K // 2)),
+            _dev(s_out, "s_out", torch.uint8, (E, N, K // 16)), _stream(stream, q.device))
+    _check(lib().moe_nvfp4_pack(*args), "moe_nvfp4_pack")
+    return q_out, s_out
+
+
+def pack_experts(experts, stream=None):
+    """Tile-major copy of a dict of row-major NVFP4 expert tensors (see experts_struct)."""
+    out = {"ts": experts["ts"]}
+    for m in ("gate", "up", "down"):
+        out[m + "_q"], out[m + "_s"] = nvfp4_pack(experts[m + "_q"], experts[m + "_s"],
+                                                  stream=stream)
+    return out
+
+
 def experts_struct(experts):
-    """ctypes struct for a dict of NVFP4 expert tensors (gate_q, up_q, down_q, gate_s, up_s,
-    down_s: uint8; ts: [E][3] float32)."""
+    """ctypes struct for a dict of tile-major NVFP4 expert tensors (gate_q, up_q, down_q,
+    gate_s, up_s, down_s: uint8 with the row-major shapes [E][N][K/2] / [E][N][K/16];
+    ts: [E][3] float32)."""
     E, I, h2 = experts["gate_q"].shape
     H = h2 * 2
     shapes = dict(gate_q=(E, I, H // 2), up_q=(E, I, H // 2), down_q=(E, H, I // 2),

@@ -163,3 +163,22 @@ MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t
   return from_hip(moe::launch_combine(y_dev, y_dtype == MOE_F16, slot_row_dev, topk_w_dev, T, k,
                                       H, out_dev, (hipStream_t)stream));
 }
+
+MOE_API moe_status moe_nvfp4_pack(const uint8_t* q_rowmajor_dev, const uint8_t* s_rowmajor_dev,
+                                  int32_t E, int32_t N, int32_t K, uint8_t* q_tiled_dev,
+                                  uint8_t* s_tiled_dev, void* stream) {
+  if (!q_rowmajor_dev || !s_rowmajor_dev || !q_tiled_dev || !s_tiled_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_rowmajor_dev) || !aligned16(s_rowmajor_dev) || !aligned16(q_tiled_dev) ||
+      !aligned16(s_tiled_dev))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N % 16 != 0 || K % 128 != 0 || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  const size_t qbytes = (size_t)E * N * K / 2, sbytes = (size_t)E * N * K / 16;
+  const uintptr_t qi = (uintptr_t)q_rowmajor_dev, qo = (uintptr_t)q_tiled_dev;
+  const uintptr_t si = (uintptr_t)s_rowmajor_dev, so = (uintptr_t)s_tiled_dev;
+  if (qi < qo + qbytes && qo < qi + qbytes) return MOE_ERR_INVALID_ARGUMENT;  // no overlap
+  if (si < so + sbytes && so < si + sbytes) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(moe::launch_pack(q_rowmajor_dev, s_rowmajor_dev, E, N, K, q_tiled_dev,
+                                   s_tiled_dev, (hipStream_t)stream));
+}

@@ -20,10 +20,12 @@ constexpr int kGroupChunk = 16384;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Router launch plan: TT tokens per block, the hidden dimension split into KS slices of kc.
+// Router launch plan: TT tokens per block (RG wavefronts), the hidden dimension split into KS
+// slices of kc rows, `tiles` token tiles.
 struct RoutePlan {
-  int TT, KS, kc;
+  int TT, RG, KS, kc, tiles;
 };
+
 RoutePlan route_plan(int T, int H, int E);
 
 // Byte offsets of every call's scratch inside the caller's workspace.
@@ -58,6 +60,9 @@ struct FfnArgs {
   _Float16* h16;  // workspace
 };
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_pack(const uint8_t* q_in, const uint8_t* s_in, int E, int N, int K,
+                       uint8_t* q_out, uint8_t* s_out, hipStream_t s);
 
 hipError_t launch_combine(const void* y, int y_f16, const int32_t* slot_row, const float* w,
                           int T, int k, int H, float* out, hipStream_t s);

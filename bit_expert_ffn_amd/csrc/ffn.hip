@@ -8,9 +8,10 @@
 // expert fits in the same row tile as a single token (Muse Spark page, section 6).
 //
 // Matrix-core mapping (gfx950, v_mfma_f32_16x16x32_f16, 64-lane wavefronts):
-//   one wavefront computes a 16 (rows) x 16 (features) tile over the full K.  K is walked in
-//   chunks of 128.  Lane l = 16*g + n holds, for chunk c, weight row n's 32 values
-//   K = [c*128 + g*32, +32): exactly one 16-byte load of packed codes plus two scale bytes.
+//   one wavefront computes a 16 (rows) x 16 (features) tile.  K is walked in chunks of 128.
+//   The weights are tile-major (see pack.hip): for a 16-feature row tile and chunk c, lane
+//   l = 16*g + n gets feature n's 32 values K = [c*128 + g*32, +32) with one 16-byte load, and
+//   the wavefront's 64 loads are one contiguous 1 KB block (plus 128 contiguous scale bytes).
 //   Those 32 values feed four MFMAs (8 each).  The MFMA sums over its 32 k positions, so the
 //   order of K inside the chunk is free; the A operand (activations) is read with the same
 //   permutation: lane l = 16*g + m supplies row m's values [c*128 + g*32 + 8i, +8) to MFMA i.
@@ -27,8 +28,6 @@ namespace moe {
 
 constexpr int kChunk = 128;         // K values per chunk
 constexpr int kTileM = 16;          // rows per tile
-constexpr int kWavesPerBlock = 4;   // one 16-feature tile per wavefront
-constexpr int kFeatPerBlock = 16 * kWavesPerBlock;
 
 __device__ inline f16x8 decode8(uint32_t q, f16x2 s) {
   const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * s;
@@ -50,15 +49,13 @@ __device__ inline f32x4 mma_chunk(f32x4 acc, const f16x8 a[4], uint4 q, uint32_t
   return acc;
 }
 
-__device__ inline void load_a(f16x8 a[4], const _Float16* p, bool valid) {
-  if (valid) {
-    const uint4* v = reinterpret_cast<const uint4*>(p);
+// A operand of one chunk for this lane (64 contiguous bytes).  Lanes whose tile row is past the
+// expert's last row load a valid row instead: an MFMA output row depends only on the same A
+// row, and those output rows are never stored, so no lane needs a branch around its loads.
+__device__ inline void load_a(f16x8 a[4], const _Float16* p) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(f16x8, v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(f16x8, v[i]);
 }
 
 __device__ inline uint32_t load_u16(const uint8_t* p) {
@@ -81,122 +78,562 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
   reinterpret_cast<f16x8*>(x16)[i] = o;
 }
 
-// Gate/up + SwiGLU.  Grid: (I / 64, max active experts).  Block: 4 wavefronts, each one
-// 16-feature tile of gate and of up for the same features, so h = silu(g) * u is formed in
-// registers.  The block walks the expert's rows 16 at a time.
-__global__ __launch_bounds__(256) void ffn_gateup_tile_kernel(
+// Gate/up + SwiGLU.  Grid: (I / 16, max active experts).  Block: KSPLIT wavefronts that split
+// the K chunks of one 16-feature tile of gate and of up (same features, so h = silu(g) * u is
+// formed in registers).  Each wavefront loads kBatch chunks (codes, scales, activations)
+// before decoding them, so several KB per wavefront are in flight.  The split partial sums are
+// added in LDS in wavefront order.  The block walks the expert's rows 16 at a time.
+constexpr int kBatch = 4;
+
+template <int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) void ffn_gateup_tile_kernel(
     const _Float16* __restrict__ x16, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ uq, const uint8_t* __restrict__ gs,
     const uint8_t* __restrict__ us, const float* __restrict__ ts,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16) {
+    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16,
+    int min_rows) {
+  __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][2][64];
   const int slot = blockIdx.y;
   if (slot >= *n_active) return;
   const int e = active[slot];
   const int rows = count[e];
+  if (rows < min_rows) return;  // a few-row expert: the VALU path takes it
   const int base = offset[e];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int f0 = blockIdx.x * kFeatPerBlock + wv * 16;
-  const size_t qrow = ((size_t)e * I + f0 + n);
-  const uint8_t* gqp = gq + qrow * (H / 2) + g * 16;
-  const uint8_t* uqp = uq + qrow * (H / 2) + g * 16;
-  const uint8_t* gsp = gs + qrow * (H / 16) + g * 2;
-  const uint8_t* usp = us + qrow * (H / 16) + g * 2;
-  const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
+  const int f0 = blockIdx.x * 16;
   const int nchunk = H / kChunk;
+  // tile-major weights: row tile blockIdx.x of expert e, chunk c at tile index (rt*nchunk + c)
+  const size_t tile0 = (size_t)blockIdx.x * nchunk;
+  const uint8_t* gqp = gq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* uqp = uq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* gsp = gs + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
+  const uint8_t* usp = us + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
+  const int per = (nchunk + KSPLIT - 1) / KSPLIT;
+  const int cb = min(nchunk, wv * per), ce = min(nchunk, cb + per);
   for (int m0 = 0; m0 < rows; m0 += kTileM) {
-    const int ra = m0 + n;  // A row of this lane (m = lane & 15)
-    const bool va = ra < rows;
-    const int tok = va ? sorted_slot[base + ra] / k : 0;
+    const int ra = min(m0 + n, rows - 1);  // A row of this lane (m = lane & 15), clamped
+    const int tok = sorted_slot[base + ra] / k;
     const _Float16* ap = x16 + (size_t)tok * H + g * 32;
     f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    for (int c = 0; c < nchunk; ++c) {
-      f16x8 a[4];
-      load_a(a, ap + c * kChunk, va);
-      const uint4 qg = *reinterpret_cast<const uint4*>(gqp + c * (kChunk / 2));
-      const uint4 qu = *reinterpret_cast<const uint4*>(uqp + c * (kChunk / 2));
-      const uint32_t sg = load_u16(gsp + c * (kChunk / 16));
-      const uint32_t su = load_u16(usp + c * (kChunk / 16));
-      accg = mma_chunk(accg, a, qg, sg);
-      accu = mma_chunk(accu, a, qu, su);
-    }
+    for (int c = cb; c < ce; c += kBatch) {
+      uint4 qg[kBatch], qu[kBatch];
+      uint32_t sg[kBatch], su[kBatch];
+      f16x8 a[kBatch][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + g * 4 + r;
-      if (m < rows) {
-        const float gv = accg[r] * tsg, uv = accu[r] * tsu;
-        const float hv = gv / (1.0f + expf(-gv)) * uv;
-        h16[(size_t)(base + m) * I + f0 + n] = (_Float16)hv;
+      for (int u = 0; u < kBatch; ++u) {
+        if (c + u < ce) {
+          const int cc = c + u;
+          qg[u] = *reinterpret_cast<const uint4*>(gqp + cc * 1024);
+          qu[u] = *reinterpret_cast<const uint4*>(uqp + cc * 1024);
+          sg[u] = load_u16(gsp + cc * 128);
+          su[u] = load_u16(usp + cc * 128);
+          load_a(a[u], ap + cc * kChunk);
+        }
       }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c + u < ce) {
+          accg = mma_chunk(accg, a[u], qg[u], sg[u]);
+          accu = mma_chunk(accu, a[u], qu[u], su[u]);
+        }
+      }
+    }
+    if (KSPLIT > 1) {
+      red[wv][0][lane] = accg;
+      red[wv][1][lane] = accu;
+      __syncthreads();
+      if (wv == 0) {
+#pragma unroll
+        for (int w = 1; w < KSPLIT; ++w) {
+          accg += red[w][0][lane];
+          accu += red[w][1][lane];
+        }
+      }
+    }
+    if (wv == 0) {
+      const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + g * 4 + r;
+        if (m < rows) {
+          const float gv = accg[r] * tsg, uv = accu[r] * tsu;
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          h16[(size_t)(base + m) * I + f0 + n] = (_Float16)hv;
+        }
+      }
+    }
+    if (KSPLIT > 1) __syncthreads();
+  }
+}
+
+// Down projection.  Grid: (H / 16, max active experts).  A = h rows (grouped order, f16).
+template <int KSPLIT, bool Y_F16>
+__global__ __launch_bounds__(64 * KSPLIT) void ffn_down_tile_kernel(
+    const _Float16* __restrict__ h16, const uint8_t* __restrict__ dq,
+    const uint8_t* __restrict__ dsc, const float* __restrict__ ts,
+    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int H, int I,
+    void* __restrict__ y, int min_rows) {
+  __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][64];
+  const int slot = blockIdx.y;
+  if (slot >= *n_active) return;
+  const int e = active[slot];
+  const int rows = count[e];
+  if (rows < min_rows) return;
+  const int base = offset[e];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int f0 = blockIdx.x * 16;
+  const int nchunk = I / kChunk;
+  const size_t tile0 = (size_t)blockIdx.x * nchunk;
+  const uint8_t* qp = dq + (size_t)e * ((size_t)H * I / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* sp = dsc + (size_t)e * ((size_t)H * I / 16) + (tile0 * 64 + lane) * 2;
+  const int per = (nchunk + KSPLIT - 1) / KSPLIT;
+  const int cb = min(nchunk, wv * per), ce = min(nchunk, cb + per);
+  for (int m0 = 0; m0 < rows; m0 += kTileM) {
+    const int ra = min(m0 + n, rows - 1);  // clamped, as in the gate/up kernel
+    const _Float16* ap = h16 + (size_t)(base + ra) * I + g * 32;
+    f32x4 acc = {0, 0, 0, 0};
+    for (int c = cb; c < ce; c += kBatch) {
+      uint4 q[kBatch];
+      uint32_t sc[kBatch];
+      f16x8 a[kBatch][4];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c + u < ce) {
+          const int cc = c + u;
+          q[u] = *reinterpret_cast<const uint4*>(qp + cc * 1024);
+          sc[u] = load_u16(sp + cc * 128);
+          load_a(a[u], ap + cc * kChunk);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (c + u < ce) acc = mma_chunk(acc, a[u], q[u], sc[u]);
+    }
+    if (KSPLIT > 1) {
+      red[wv][lane] = acc;
+      __syncthreads();
+      if (wv == 0) {
+#pragma unroll
+        for (int w = 1; w < KSPLIT; ++w) acc += red[w][lane];
+      }
+    }
+    if (wv == 0) {
+      const float tsd = ts[e * 3 + 2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + g * 4 + r;
+        if (m < rows) {
+          const float v = acc[r] * tsd;
+          const size_t o = (size_t)(base + m) * H + f0 + n;
+          if (Y_F16)
+            reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
+          else
+            reinterpret_cast<float*>(y)[o] = v;
+        }
+      }
+    }
+    if (KSPLIT > 1) __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Few-row experts (at most R rows): VALU dot products.  A step's experts are sorted by row
+// count and the few-row ones run in their own loop, apart from the busy experts' path
+// ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", section 5 "Keeping register
+// pressure off the common path"); most experts of a decode step serve one or two rows.
+// Block: 4 wavefronts, one 16-feature tile each, over the whole K.  The expert's activation
+// rows are staged once in LDS; each lane keeps up to 2 * kSet chunks of packed weights in
+// flight: two register sets alternate, one loading while the other is used.  Lane l = 16*g + n
+// decodes its 32 values of feature n per chunk and dots them with the matching 32 activation
+// values of each row (two 16-value blocks, each block's sum times its e4m3 scale); the four
+// K-groups of a feature are added by two cross-lane shuffles in a fixed order.
+constexpr int kSet = 4;  // chunks per load set; two sets alternate
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// 8 values of one code dword dotted with 8 activations (4 pairs), accumulated into acc
+__device__ inline float dot8_bf16(uint32_t q, uint4 xx, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0),
+                                        __builtin_bit_cast(bf16x2_t, xx.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1),
+                                        __builtin_bit_cast(bf16x2_t, xx.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2),
+                                        __builtin_bit_cast(bf16x2_t, xx.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3),
+                                        __builtin_bit_cast(bf16x2_t, xx.w), acc, false);
+  return acc;
+}
+
+__device__ inline float dot8_f16(uint32_t q, uint4 xx, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0),
+                               __builtin_bit_cast(f16x2, xx.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1),
+                               __builtin_bit_cast(f16x2, xx.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2),
+                               __builtin_bit_cast(f16x2, xx.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3),
+                               __builtin_bit_cast(f16x2, xx.w), acc, false);
+  return acc;
+}
+
+// A lane's 32 values (two 16-value scale blocks): each block's dot times its e4m3 scale.
+__device__ inline float dot32_bf16(uint4 q, uint32_t sbytes, const uint4* xv) {
+  const float b0 = dot8_bf16(q.y, xv[1], dot8_bf16(q.x, xv[0], 0.f));
+  const float b1 = dot8_bf16(q.w, xv[3], dot8_bf16(q.z, xv[2], 0.f));
+  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
+         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
+}
+
+__device__ inline float dot32_f16(uint4 q, uint32_t sbytes, const uint4* xv) {
+  const float b0 = dot8_f16(q.y, xv[1], dot8_f16(q.x, xv[0], 0.f));
+  const float b1 = dot8_f16(q.w, xv[3], dot8_f16(q.z, xv[2], 0.f));
+  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
+         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
+}
+
+// the four K-groups of feature n (lanes n, n+16, n+32, n+48), fixed order
+__device__ inline float sum_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int R, int KS>
+__global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ gq,
+    const uint8_t* __restrict__ uq, const uint8_t* __restrict__ gs,
+    const uint8_t* __restrict__ us, const float* __restrict__ ts,
+    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [R][H] bf16
+  __shared__ float red[4][R][2][16];
+  const int slot = blockIdx.y;
+  if (slot >= *n_active) return;
+  const int e = active[slot];
+  const int rows = count[e];
+  if (rows > R) return;  // a busy expert: the matrix-core path takes it
+  const int base = offset[e];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int ks = wv % KS;  // this wavefront's K slice of its tile
+  // stage the expert's activation rows
+  for (int r = 0; r < rows; ++r) {
+    const int tok = sorted_slot[base + r] / k;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok * H);
+    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)r * H);
+    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
+  }
+  __syncthreads();
+  const int rt = blockIdx.x * (4 / KS) + wv / KS;  // 16-feature row tile
+  const int nchunk_all = H / kChunk;
+  // balanced split: the host keeps KS <= nchunk_all, so every slice has at least one chunk
+  const int cbeg = ks * nchunk_all / KS;
+  const int nchunk = (ks + 1) * nchunk_all / KS - cbeg;  // chunks of this slice
+  const size_t tile0 = (size_t)rt * nchunk_all + cbeg;
+  const uint8_t* gqp = gq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* uqp = uq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* gsp = gs + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
+  const uint8_t* usp = us + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
+  // two sets of kSet chunks alternate: one set's loads are in flight while the other is used
+  uint4 qgA[kSet], quA[kSet], qgB[kSet], quB[kSet];
+  uint32_t sgA[kSet], suA[kSet], sgB[kSet], suB[kSet];
+  auto load_set = [&](uint4* qg, uint4* qu, uint32_t* sg, uint32_t* su, int c0) {
+#pragma unroll
+    for (int u = 0; u < kSet; ++u) {
+      const int c = min(c0 + u, nchunk - 1);  // clamped: past the end re-reads the last chunk
+      qg[u] = *reinterpret_cast<const uint4*>(gqp + c * 1024);
+      qu[u] = *reinterpret_cast<const uint4*>(uqp + c * 1024);
+      sg[u] = load_u16(gsp + c * 128);
+      su[u] = load_u16(usp + c * 128);
+    }
+  };
+  float ag[R], au[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) ag[r] = au[r] = 0.f;
+  auto use_set = [&](const uint4* qg, const uint4* qu, const uint32_t* sg, const uint32_t* su,
+                     int c0) {
+#pragma unroll
+    for (int u = 0; u < kSet; ++u) {
+      const int c = c0 + u;
+      if (c < nchunk) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r < rows) {
+            const uint4* xv = reinterpret_cast<const uint4*>(xs + (size_t)r * H + (cbeg + c) * kChunk + g * 32);
+            ag[r] += dot32_bf16(qg[u], sg[u], xv);
+            au[r] += dot32_bf16(qu[u], su[u], xv);
+          }
+        }
+      }
+    }
+  };
+  load_set(qgA, quA, sgA, suA, 0);
+  for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
+    load_set(qgB, quB, sgB, suB, c0 + kSet);
+    use_set(qgA, quA, sgA, suA, c0);
+    load_set(qgA, quA, sgA, suA, c0 + 2 * kSet);
+    use_set(qgB, quB, sgB, suB, c0 + kSet);
+  }
+  // K-groups of a feature (cross-lane), then the block's K slices in order (LDS)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) {
+      ag[r] = sum_groups(ag[r]);
+      au[r] = sum_groups(au[r]);
+      if (KS > 1 && g == 0) {
+        red[wv][r][0][n] = ag[r];
+        red[wv][r][1][n] = au[r];
+      }
+    }
+  }
+  if (KS > 1) {
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < rows) {
+        float sg2 = red[wv][r][0][n], su2 = red[wv][r][1][n];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) {
+          sg2 += red[wv + j][r][0][n];
+          su2 += red[wv + j][r][1][n];
+        }
+        ag[r] = sg2;
+        au[r] = su2;
+      }
+    }
+  }
+  const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows && g == 0) {
+      const float gv = ag[r] * tsg, uv = au[r] * tsu;
+      const float hv = gv / (1.0f + expf(-gv)) * uv;
+      h16[(size_t)(base + r) * I + rt * 16 + n] = (_Float16)hv;
     }
   }
 }
 
-// Down projection.  Grid: (H / 64, max active experts).  A = h rows (grouped order, f16).
-template <bool Y_F16>
-__global__ __launch_bounds__(256) void ffn_down_tile_kernel(
+template <int R, int KS, bool Y_F16>
+__global__ __launch_bounds__(256) void ffn_down_few_kernel(
     const _Float16* __restrict__ h16, const uint8_t* __restrict__ dq,
     const uint8_t* __restrict__ dsc, const float* __restrict__ ts,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int H, int I,
     void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t hs[];  // [R][I] f16
+  __shared__ float red[4][R][16];
   const int slot = blockIdx.y;
   if (slot >= *n_active) return;
   const int e = active[slot];
   const int rows = count[e];
+  if (rows > R) return;
   const int base = offset[e];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int f0 = blockIdx.x * kFeatPerBlock + wv * 16;
-  const size_t qrow = ((size_t)e * H + f0 + n);
-  const uint8_t* qp = dq + qrow * (I / 2) + g * 16;
-  const uint8_t* sp = dsc + qrow * (I / 16) + g * 2;
-  const float tsd = ts[e * 3 + 2];
-  const int nchunk = I / kChunk;
-  for (int m0 = 0; m0 < rows; m0 += kTileM) {
-    const int ra = m0 + n;
-    const bool va = ra < rows;
-    const _Float16* ap = h16 + (size_t)(base + (va ? ra : 0)) * I + g * 32;
-    f32x4 acc = {0, 0, 0, 0};
-    for (int c = 0; c < nchunk; ++c) {
-      f16x8 a[4];
-      load_a(a, ap + c * kChunk, va);
-      const uint4 q = *reinterpret_cast<const uint4*>(qp + c * (kChunk / 2));
-      const uint32_t s = load_u16(sp + c * (kChunk / 16));
-      acc = mma_chunk(acc, a, q, s);
-    }
+  const int ks = wv % KS;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(h16 + (size_t)base * I);
+    uint4* dst = reinterpret_cast<uint4*>(hs);
+    for (int i = threadIdx.x; i < rows * I / 8; i += 256) dst[i] = src[i];
+  }
+  __syncthreads();
+  const int rt = blockIdx.x * (4 / KS) + wv / KS;
+  const int nchunk_all = I / kChunk;
+  const int cbeg = ks * nchunk_all / KS;
+  const int nchunk = (ks + 1) * nchunk_all / KS - cbeg;
+  const size_t tile0 = (size_t)rt * nchunk_all + cbeg;
+  const uint8_t* qp = dq + (size_t)e * ((size_t)H * I / 2) + (tile0 * 64 + lane) * 16;
+  const uint8_t* sp = dsc + (size_t)e * ((size_t)H * I / 16) + (tile0 * 64 + lane) * 2;
+  uint4 qA[kSet], qB[kSet];
+  uint32_t sA[kSet], sB[kSet];
+  auto load_set = [&](uint4* q, uint32_t* sc, int c0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + g * 4 + r;
-      if (m < rows) {
-        const float v = acc[r] * tsd;
-        const size_t o = (size_t)(base + m) * H + f0 + n;
-        if (Y_F16)
-          reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
-        else
-          reinterpret_cast<float*>(y)[o] = v;
+    for (int u = 0; u < kSet; ++u) {
+      const int c = min(c0 + u, nchunk - 1);
+      q[u] = *reinterpret_cast<const uint4*>(qp + c * 1024);
+      sc[u] = load_u16(sp + c * 128);
+    }
+  };
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  auto use_set = [&](const uint4* q, const uint32_t* sc, int c0) {
+#pragma unroll
+    for (int u = 0; u < kSet; ++u) {
+      const int c = c0 + u;
+      if (c < nchunk) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (r < rows)
+            acc[r] += dot32_f16(q[u], sc[u], reinterpret_cast<const uint4*>(hs + (size_t)r * I + (cbeg + c) * kChunk + g * 32));
       }
+    }
+  };
+  load_set(qA, sA, 0);
+  for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
+    load_set(qB, sB, c0 + kSet);
+    use_set(qA, sA, c0);
+    load_set(qA, sA, c0 + 2 * kSet);
+    use_set(qB, sB, c0 + kSet);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) {
+      acc[r] = sum_groups(acc[r]);
+      if (KS > 1 && g == 0) red[wv][r][n] = acc[r];
+    }
+  }
+  if (KS > 1) {
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < rows) {
+        float v = red[wv][r][n];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) v += red[wv + j][r][n];
+        acc[r] = v;
+      }
+    }
+  }
+  const float tsd = ts[e * 3 + 2];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < rows && g == 0) {
+      const float v = acc[r] * tsd;
+      const size_t o = (size_t)(base + r) * H + rt * 16 + n;
+      if (Y_F16)
+        reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
+      else
+        reinterpret_cast<float*>(y)[o] = v;
     }
   }
 }
 
+static int pick_ksplit(int blocks, int nchunk) {
+  int ks = (6144 + blocks - 1) / blocks;
+  if (ks > 4) ks = 4;
+  if (ks > nchunk) ks = nchunk;
+  if (ks >= 4) return 4;
+  if (ks >= 2) return 2;
+  return 1;
+}
+
+// Rows per expert handled by the few-row path for a given token count (0: none).  An expert
+// has at most T rows (a token's k experts are distinct).  The LDS staging of the activation
+// rows bounds R * K * 2 bytes to 64 KB.
+// K slices per 16-feature tile in the few-row kernels: enough wavefronts (and bytes in flight)
+// to cover the HBM latency when there are few tiles.
+static int few_ksplit(int tiles, int nchunk) {
+  int ks = tiles <= 2048 ? 4 : tiles <= 4096 ? 2 : 1;
+  while (ks > nchunk) ks >>= 1;  // every K slice keeps at least one chunk
+  return ks;
+}
+
+static int few_rows(int T, int H, int I) {
+  int R = T <= 1 ? 1 : T <= 2 ? 2 : 4;
+  const int kmax = H > I ? H : I;
+  while (R > 0 && (size_t)R * kmax * 2 > 65536) R >>= 1;
+  return R;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const int maxe = a.E < a.T * a.k ? a.E : a.T * a.k;
-  const size_t n8 = (size_t)a.T * a.H / 8;
-  x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(a.x, a.x16, n8);
-  ffn_gateup_tile_kernel<<<dim3(a.I / kFeatPerBlock, maxe), 256, 0, s>>>(
-      a.x16, a.gq, a.uq, a.gs, a.us, a.ts, a.count, a.offset, a.sorted_slot, a.active,
-      a.n_active, a.k, a.H, a.I, a.h16);
-  if (a.y_f16)
-    ffn_down_tile_kernel<true><<<dim3(a.H / kFeatPerBlock, maxe), 256, 0, s>>>(
-        a.h16, a.dq, a.ds, a.ts, a.count, a.offset, a.active, a.n_active, a.H, a.I, a.y);
-  else
-    ffn_down_tile_kernel<false><<<dim3(a.H / kFeatPerBlock, maxe), 256, 0, s>>>(
-        a.h16, a.dq, a.ds, a.ts, a.count, a.offset, a.active, a.n_active, a.H, a.I, a.y);
+  const int R = few_rows(a.T, a.H, a.I);
+  const bool heavy = a.T > R;  // some expert may have more than R rows
+  if (heavy) {
+    const size_t n8 = (size_t)a.T * a.H / 8;
+    x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(a.x, a.x16, n8);
+  }
+  // gate/up + SwiGLU
+  if (R > 0) {
+    const int ks = few_ksplit(maxe * (a.I / 16), a.H / kChunk);
+    const dim3 grid(a.I / 16 / (4 / ks), maxe);
+    const size_t lds = (size_t)R * a.H * 2;
+#define MOE_FEW_GU(R_, KS_)                                                                  \
+  ffn_gateup_few_kernel<R_, KS_><<<grid, 256, lds, s>>>(a.x, a.gq, a.uq, a.gs, a.us, a.ts,   \
+                                                        a.count, a.offset, a.sorted_slot,    \
+                                                        a.active, a.n_active, a.k, a.H, a.I, \
+                                                        a.h16)
+#define MOE_FEW_GU_R(R_)                 \
+  do {                                   \
+    if (ks == 4) MOE_FEW_GU(R_, 4);      \
+    else if (ks == 2) MOE_FEW_GU(R_, 2); \
+    else MOE_FEW_GU(R_, 1);              \
+  } while (0)
+    if (R == 1) MOE_FEW_GU_R(1);
+    else if (R == 2) MOE_FEW_GU_R(2);
+    else MOE_FEW_GU_R(4);
+#undef MOE_FEW_GU_R
+#undef MOE_FEW_GU
+  }
+  if (heavy) {
+    const int ksg = pick_ksplit(maxe * (a.I / 16), a.H / kChunk);
+    const dim3 gg(a.I / 16, maxe);
+#define MOE_GATEUP(KS_)                                                                   \
+  ffn_gateup_tile_kernel<KS_><<<gg, 64 * KS_, 0, s>>>(a.x16, a.gq, a.uq, a.gs, a.us, a.ts, \
+                                                      a.count, a.offset, a.sorted_slot,    \
+                                                      a.active, a.n_active, a.k, a.H, a.I, \
+                                                      a.h16, R + 1)
+    if (ksg == 4) MOE_GATEUP(4);
+    else if (ksg == 2) MOE_GATEUP(2);
+    else MOE_GATEUP(1);
+#undef MOE_GATEUP
+  }
+  // down
+  if (R > 0) {
+    const int ks = few_ksplit(maxe * (a.H / 16), a.I / kChunk);
+    const dim3 grid(a.H / 16 / (4 / ks), maxe);
+    const size_t lds = (size_t)R * a.I * 2;
+#define MOE_FEW_D(R_, KS_, F16_)                                                                 \
+  ffn_down_few_kernel<R_, KS_, F16_><<<grid, 256, lds, s>>>(a.h16, a.dq, a.ds, a.ts, a.count,    \
+                                                            a.offset, a.active, a.n_active, a.H, \
+                                                            a.I, a.y)
+#define MOE_FEW_D_R(R_, F16_)                   \
+  do {                                          \
+    if (ks == 4) MOE_FEW_D(R_, 4, F16_);        \
+    else if (ks == 2) MOE_FEW_D(R_, 2, F16_);   \
+    else MOE_FEW_D(R_, 1, F16_);                \
+  } while (0)
+    if (a.y_f16) {
+      if (R == 1) MOE_FEW_D_R(1, true);
+      else if (R == 2) MOE_FEW_D_R(2, true);
+      else MOE_FEW_D_R(4, true);
+    } else {
+      if (R == 1) MOE_FEW_D_R(1, false);
+      else if (R == 2) MOE_FEW_D_R(2, false);
+      else MOE_FEW_D_R(4, false);
+    }
+#undef MOE_FEW_D_R
+#undef MOE_FEW_D
+  }
+  if (heavy) {
+    const int ksd = pick_ksplit(maxe * (a.H / 16), a.I / kChunk);
+    const dim3 gd(a.H / 16, maxe);
+#define MOE_DOWN(KS_, F16_)                                                                    \
+  ffn_down_tile_kernel<KS_, F16_><<<gd, 64 * KS_, 0, s>>>(a.h16, a.dq, a.ds, a.ts, a.count,   \
+                                                          a.offset, a.active, a.n_active, a.H, \
+                                                          a.I, a.y, R + 1)
+    if (a.y_f16) {
+      if (ksd == 4) MOE_DOWN(4, true);
+      else if (ksd == 2) MOE_DOWN(2, true);
+      else MOE_DOWN(1, true);
+    } else {
+      if (ksd == 4) MOE_DOWN(4, false);
+      else if (ksd == 2) MOE_DOWN(2, false);
+      else MOE_DOWN(1, false);
+    }
+#undef MOE_DOWN
+  }
   return hipGetLastError();
 }
 

@@ -95,17 +95,25 @@ __device__ inline void wave_scan_offsets(const int* cnt, int E, int* off) {
   if (lane == 63) off[E] = incl;
 }
 
-// Active experts by (count desc, id asc); thread e places expert e.  Needs >= E threads.
+// Active experts by (count desc, id asc); thread e places expert e.  Needs >= E threads and
+// cnt[] zero-filled up to kMaxExperts (read 4 at a time).
 __device__ inline void place_active(const int* cnt, int E, int32_t* __restrict__ active,
                                     int32_t* __restrict__ n_active) {
   const int e = threadIdx.x;
   if (e >= E) return;
   const int c = cnt[e];
   int rank = 0, nact = 0;
-  for (int j = 0; j < E; ++j) {
-    const int cj = cnt[j];
-    nact += cj > 0;
-    rank += (cj > c) || (cj == c && j < e);
+  const int4* c4 = reinterpret_cast<const int4*>(cnt);
+  const int n4 = (E + 3) >> 2;
+#pragma unroll 8
+  for (int j4 = 0; j4 < n4; ++j4) {
+    const int4 v = c4[j4];
+    const int j = j4 * 4;
+    nact += (v.x > 0) + (v.y > 0) + (v.z > 0) + (v.w > 0);
+    rank += (v.x > c) || (v.x == c && j < e);
+    rank += (v.y > c) || (v.y == c && j + 1 < e);
+    rank += (v.z > c) || (v.z == c && j + 2 < e);
+    rank += (v.w > c) || (v.w == c && j + 3 < e);
   }
   if (c > 0) active[rank] = e;
   if (e >= nact) active[e] = -1;
@@ -117,37 +125,92 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
     int32_t* __restrict__ offset, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
   __shared__ int wcnt[kGroupWaves][kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint32_t key[kMaxExperts];
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
+  __shared__ int rank[kMaxExperts];
+  __shared__ int s_nact;
+  __shared__ int32_t sids[kGroupSmallMax];  // the expert ids, read from global memory once
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
+  for (int i = tid; i < n; i += 1024) sids[i] = ids[i];
   for (int i = tid; i < kGroupWaves * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
+  if (tid < kMaxExperts) {
+    cnt[tid] = 0;
+    rank[tid] = 0;
+    key[tid] = 0;
+  }
+  if (tid == 0) s_nact = 0;
   __syncthreads();
   const int per = (n + kGroupWaves - 1) / kGroupWaves;
   const int s0 = min(n, wv * per), s1 = min(n, s0 + per);
-  wave_hist(ids, s0, s1, wcnt[wv]);
+  wave_hist(sids, s0, s1, wcnt[wv]);
   __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int w = 0; w < kGroupWaves; ++w) {
-      const int c = wcnt[w][tid];
-      wcnt[w][tid] = run;
-      run += c;
+  // per expert: exclusive scan of the 16 wavefront counts.  Thread (e, q) owns wavefronts
+  // 4q..4q+3 of expert e; the 4 threads of an expert are adjacent lanes.
+  const int q = tid & 3, ex = tid >> 2;
+  {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = ex < E ? wcnt[4 * q + i][ex] : 0;
+      sum += c[i];
     }
-    cnt[tid] = run;
+    int incl = sum;
+    int v = __shfl_up(incl, 1, 4);
+    if (q >= 1) incl += v;
+    v = __shfl_up(incl, 2, 4);
+    if (q >= 2) incl += v;
+    const int total = __shfl(incl, 3, 4);
+    int run = incl - sum;
+    if (ex < E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wcnt[4 * q + i][ex] = run;
+        run += c[i];
+      }
+      if (q == 0) cnt[ex] = total;
+    }
   }
   __syncthreads();
   if (wv == 0) wave_scan_offsets(cnt, E, off);
   __syncthreads();
-  if (tid < E) {
-    for (int w = 0; w < kGroupWaves; ++w) wcnt[w][tid] += off[tid];
-    count[tid] = cnt[tid];
-    offset[tid] = off[tid];
-    if (tid == 0) offset[E] = off[E];
+  if (ex < E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wcnt[4 * q + i][ex] += off[ex];
+    if (q == 0) {
+      count[ex] = cnt[ex];
+      offset[ex] = off[ex];
+      // ranking key: larger key = earlier in the active list (count desc, then id asc);
+      // counts are <= n <= 16384 < 2^24
+      key[ex] = ((uint32_t)cnt[ex] << 8) | (uint32_t)(255 - ex);
+      if (ex == 0) offset[E] = off[E];
+    }
   }
   __syncthreads();
-  wave_scatter(ids, s0, s1, E, wcnt[wv], sorted_slot, slot_row);
-  place_active(cnt, E, active, n_active);
+  wave_scatter(sids, s0, s1, E, wcnt[wv], sorted_slot, slot_row);
+  // rank of expert e = number of larger keys; thread (e, seg) counts over 64 keys
+  {
+    const int e = tid & 255, seg = tid >> 8;
+    const uint32_t ke = key[e];
+    int r = 0, na = 0;
+    const uint4* k4 = reinterpret_cast<const uint4*>(key + seg * 64);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 kk = k4[j];
+      r += (kk.x > ke) + (kk.y > ke) + (kk.z > ke) + (kk.w > ke);
+      na += (kk.x > 255u) + (kk.y > 255u) + (kk.z > 255u) + (kk.w > 255u);
+    }
+    if (e < E && ke > 255u) atomicAdd(&rank[e], r);
+    if (e == 0) atomicAdd(&s_nact, na);
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int nact = s_nact;
+    if (key[tid] > 255u) active[rank[tid]] = tid;
+    if (tid >= nact) active[tid] = -1;
+    if (tid == 0) *n_active = nact;
+  }
 }
 
 // Pass 1: per-wavefront histograms of each block's kGroupChunk slots -> whist[blk*16+w][E].
@@ -174,11 +237,14 @@ __global__ __launch_bounds__(256) void group_scan_kernel(int32_t* __restrict__ w
                                                          int32_t* __restrict__ offset,
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ n_active) {
-  __shared__ int cnt[kMaxExperts];
+  __shared__ __attribute__((aligned(16))) int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   const int tid = threadIdx.x;
+  cnt[tid] = 0;  // 256 threads
+  __syncthreads();
   if (tid < E) {
     int run = 0;
+#pragma unroll 8
     for (int w = 0; w < nw; ++w) {
       const int c = whist[(size_t)w * E + tid];
       whist[(size_t)w * E + tid] = run;

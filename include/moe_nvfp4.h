@@ -68,13 +68,23 @@ enum {
 /* element type tag of the expert-output buffer y */
 enum { MOE_F32 = 0, MOE_F16 = 1 };
 
-/* NVFP4 expert weights.  All pointers are device pointers.  For every expert e:
- *   gate_q, up_q [E][I][H/2]  e2m1 codes, two per byte, low nibble = even k (k runs over H)
- *   gate_s, up_s [E][I][H/16] e4m3 (OCP E4M3FN) scale codes, one per 16 consecutive k of a row
- *   down_q       [E][H][I/2]  e2m1 codes, k runs over I
- *   down_s       [E][H][I/16] e4m3 scale codes
- *   tensor_scale [E][3]       fp32 scales of gate, up and down
- * Weight value: W[n][k] = e2m1(code) * e4m3(scale of block k/16) * tensor_scale.
+/* NVFP4 expert weights, as moe_expert_ffn_nvfp4 reads them.  All pointers are device
+ * pointers.  Per expert e there are three matrices W[n][k] with N rows (outputs) and K columns
+ * (the reduction):  gate and up (N = I, K = H) and down (N = H, K = I).  Weight value:
+ *     W[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k / 16]) * tensor_scale[e][matrix]
+ * with e2m1 codes (4 bits) and OCP E4M3FN scale codes, one scale per 16 consecutive k.
+ * Byte layout: TILE-MAJOR (moe_nvfp4_pack converts the usual row-major layout, codes [N][K/2]
+ * with the low nibble holding the even k, and scales [N][K/16]).  The matrix is cut into
+ * 16-row x 128-column tiles (r = n / 16, c = k / 128), ordered r-major; inside a tile, slot
+ * l = 16 * ((k % 128) / 32) + n % 16 holds the 32 codes of row n, columns 128c + 32g .. +32
+ * (16 bytes, low nibble = even k) and their two scale bytes:
+ *     code byte  of (n, k): ((r * (K/128) + c) * 64 + l) * 16 + (k % 32) / 2
+ *     scale byte of (n, k): ((r * (K/128) + c) * 64 + l) * 2  + (k % 32) / 16
+ * Expert e's matrix starts at byte e * N*K/2 (codes) and e * N*K/16 (scales), i.e.
+ *   gate_q, up_q [E] x I*H/2 bytes,  gate_s, up_s [E] x I*H/16 bytes,
+ *   down_q       [E] x H*I/2 bytes,  down_s       [E] x H*I/16 bytes,
+ *   tensor_scale [E][3] fp32 (gate, up, down).
+ * One wavefront load then reads one tile: 1 KB of codes or 128 B of scales, contiguous.
  * The struct itself is host memory, read during the call only. */
 typedef struct moe_nvfp4_experts {
   const uint8_t *gate_q, *up_q, *down_q;
@@ -90,7 +100,9 @@ int32_t moe_abi_version(void);
 const char *moe_status_string(moe_status status);
 
 /* Bytes of device workspace that every call of a layer with these sizes needs (one buffer
- * serves all four calls).  Returns 0 if the sizes are outside the shape limits. */
+ * serves all four calls, which must then be ordered on one stream).  Returns 0 if the sizes are
+ * outside the shape limits.  The contents are scratch: no initialisation is needed and calls
+ * keep nothing in it from one call to the next. */
 size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /* Router and top-k ("The model": every token is routed to k of E experts).
@@ -136,6 +148,15 @@ moe_status moe_expert_ffn_nvfp4(const void *x_dev, const moe_nvfp4_experts *w, c
                                 const int32_t *active_dev, const int32_t *n_active_dev, int32_t T,
                                 int32_t k, void *y_dev, int32_t y_dtype, void *ws_dev,
                                 size_t ws_bytes, void *stream);
+
+/* Layout conversion for NVFP4 weights: E matrices [N][K] from row-major (codes [E][N][K/2],
+ * low nibble = even k; scales [E][N][K/16]) to the tile-major layout moe_expert_ffn_nvfp4
+ * reads (see moe_nvfp4_experts).  Run once per matrix kind when weights are loaded: gate and
+ * up with (N, K) = (I, H), down with (N, K) = (H, I).  Input and output must not overlap.
+ * Requires N % 16 == 0, K % 128 == 0, N, K <= 65536.  Asynchronous on `stream`. */
+moe_status moe_nvfp4_pack(const uint8_t *q_rowmajor_dev, const uint8_t *s_rowmajor_dev,
+                          int32_t E, int32_t N, int32_t K, uint8_t *q_tiled_dev,
+                          uint8_t *s_tiled_dev, void *stream);
 
 /* Routing-weighted combine (Muse Spark page, section 8, "A one-pass combine"; "No zero fill"):
  *   out[t][n] = sum over j = 0..k-1 of topk_w[t][j] * y[slot_row[t*k+j]][n], in fp32.

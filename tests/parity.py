@@ -86,7 +86,7 @@ def gpu_layer(L, k, y_dtype=torch.float32, device="cuda"):
     import bit_expert_ffn_amd as moe
     x = L["x"].to(device)
     T, H = x.shape
-    ex = {n: v.to(device) for n, v in L["experts"].items()}
+    ex = moe.pack_experts({n: v.to(device) for n, v in L["experts"].items()})
     E, I = ex["gate_q"].shape[0], ex["gate_q"].shape[1]
     buf = moe.LayerBuffers(T, H, I, E, k, device=device, y_dtype=y_dtype)
     bias = None if L["bias"] is None else L["bias"].to(device)
@@ -99,6 +99,23 @@ def np_buf(buf):
     return {n: getattr(buf, n).cpu().numpy() for n in
             ("logits", "topk_id", "topk_w", "count", "offset", "sorted_slot", "slot_row",
              "active", "n_active", "out")} | {"y": buf.y.float().cpu().numpy()}
+
+
+def tile_major_np(q, s):
+    """Reference of the tile-major layout, written from its offset formula (numpy)."""
+    E, N, k2 = q.shape
+    K = k2 * 2
+    qo = np.empty(E * N * K // 2, np.uint8)
+    so = np.empty(E * N * K // 16, np.uint8)
+    for e in range(E):
+        for n in range(N):
+            for c in range(K // 128):
+                for g in range(4):
+                    l = 16 * g + n % 16
+                    t = (n // 16) * (K // 128) + c
+                    qo[e * N * K // 2 + (t * 64 + l) * 16:][:16] = q[e, n, c * 64 + g * 16:][:16]
+                    so[e * N * K // 16 + (t * 64 + l) * 2:][:2] = s[e, n, c * 8 + g * 2:][:2]
+    return qo.reshape(q.shape), so.reshape(s.shape)
 
 
 def experts_np(ex):

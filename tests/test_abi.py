@@ -132,3 +132,15 @@ def test_python_binding_validates_before_calling():
     with pytest.raises(ValueError):
         moe.route(x, torch.zeros(256, 8), None, 2, torch.zeros(4, 2, dtype=torch.int32),
                   torch.zeros(4, 2), torch.zeros(16, dtype=torch.uint8))
+
+
+def test_pack_rejects_bad_arguments():
+    p = moe.lib().moe_nvfp4_pack
+    B = A + (1 << 40)  # a second, non-overlapping fake region
+    C, D = A + (2 << 40), A + (3 << 40)
+    assert p(None, A, 2, 16, 128, B, C, None) == INVALID
+    assert p(A, B, 2, 16, 128, C + 4, D, None) == INVALID
+    assert p(A, B, 0, 16, 128, C, D, None) == INVALID
+    assert p(A, B, 2, 24, 128, C, D, None) == SHAPE
+    assert p(A, B, 2, 16, 96, C, D, None) == SHAPE
+    assert p(A, B, 2, 16, 128, A, D, None) == INVALID  # in place

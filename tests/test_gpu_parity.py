@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 from parity import (check_out, check_routing, experts_np, gpu_layer, np_buf, oracle_token_out,
-                    LOGIT_TOL, out_errors)
+                    tile_major_np, LOGIT_TOL, out_errors)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +21,9 @@ SHAPES = {
     "single_expert": dict(T=33, H=256, I=256, E=1, k=1, router="normal", zipf=None),
     "dense_k_eq_e": dict(T=6, H=256, I=128, E=8, k=8, router="normal", zipf=None),
     "zipf_skew": dict(T=96, H=256, I=256, E=64, k=8, router="normal", zipf=1.1),
+    "one_token": dict(T=1, H=1024, I=256, E=32, k=8, router="normal", zipf=None),
+    "two_tokens": dict(T=2, H=512, I=384, E=16, k=4, router="normal", zipf=None),
+    "one_token_wide": dict(T=1, H=7168, I=256, E=8, k=2, router="normal", zipf=None),
 }
 
 
@@ -102,7 +105,7 @@ def test_group_stage_bit_exact(T, k, E):
     rng = np.random.default_rng(T + k)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     ref = oracle.group(ids, E)
-    ws = torch.empty(max(256, moe.workspace_size(T, 128, 128, E, k)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_size(T, 128, 128, E, k), dtype=torch.uint8, device="cuda")
     out = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
            (("count", E), ("offset", E + 1), ("sorted_slot", T * k), ("slot_row", T * k),
             ("active", E), ("n_active", 1))}
@@ -125,9 +128,9 @@ def test_ffn_and_combine_stages_on_oracle_inputs():
     grp = oracle.group(ids, sp["E"])
     y_ref = oracle.ffn(N["x"], ex, grp, k)
     x = L["x"].cuda()
-    exd = {n: v.cuda() for n, v in L["experts"].items()}
+    exd = moe.pack_experts({n: v.cuda() for n, v in L["experts"].items()})
     T, H = x.shape
-    ws = torch.empty(moe.workspace_size(T, H, sp["I"], sp["E"], k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_size(T, H, sp["I"], sp["E"], k), dtype=torch.uint8, device="cuda")
     y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
     moe.expert_ffn_nvfp4(x, exd, _dev_i32(grp["count"]), _dev_i32(grp["offset"]),
                          _dev_i32(grp["sorted_slot"]), _dev_i32(grp["active"]),
@@ -154,8 +157,21 @@ def test_route_stage_zero_input_and_ties():
     wr = torch.randn((H, E), device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(moe.workspace_size(T, H, 128, E, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(moe.workspace_size(T, H, 128, E, k), dtype=torch.uint8, device="cuda")
     moe.route(x, wr, None, k, ids, w, ws)
     torch.cuda.synchronize()
     assert ids.cpu().tolist() == [list(range(k))] * T
     assert torch.all(w.cpu() == 1.0 / k)
+
+
+@pytest.mark.parametrize("E,N,K", [(2, 16, 128), (3, 48, 384), (1, 256, 256)])
+def test_pack_tile_major_bit_exact(E, N, K):
+    import bit_expert_ffn_amd as moe
+    g = torch.Generator().manual_seed(E * N + K)
+    q = torch.randint(0, 256, (E, N, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    s = torch.randint(0, 256, (E, N, K // 16), generator=g, dtype=torch.int32).to(torch.uint8)
+    qo, so = moe.nvfp4_pack(q.cuda(), s.cuda())
+    torch.cuda.synchronize()
+    rq, rs = tile_major_np(q.numpy(), s.numpy())
+    assert np.array_equal(qo.cpu().numpy(), rq)
+    assert np.array_equal(so.cpu().numpy(), rs)
