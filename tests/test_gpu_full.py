@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
+the whole layer runs on every token; the CPU oracle recomputes a sample of tokens one by one
+(routing and FFN are per token, so a sampled token's output is exact), and the grouping arrays
+are checked by invariants that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import LOGIT_TOL, check_out, check_routing, oracle_token_out
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _layer(name):
+    """Inputs generated on the GPU (as the benchmark does) plus host copies for the oracle."""
+    if name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        sp = dict(synth.SPECS[name])
+        T = sp["T"] * (4 if sp["T"] == 1 else 1)  # decode: a few pool tokens, one call each
+        L = synth.make_layer(sp, seed=0, device="cuda", T=T)
+        ex_host = oracle.Experts(**{n: v.cpu().numpy() for n, v in L["experts"].items()})
+        _cache[name] = (sp, L, ex_host)
+    return _cache[name]
+
+
+def _run(L, x, k):
+    import bit_expert_ffn_amd as moe
+    T, H = x.shape
+    ex = L.setdefault("_packed", None) or moe.pack_experts(L["experts"])
+    L["_packed"] = ex
+    E, I = ex["gate_q"].shape[0], ex["gate_q"].shape[1]
+    buf = moe.LayerBuffers(T, H, I, E, k, device="cuda")
+    moe.layer(x, L["w_router"], L["bias"], ex, k, buf)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _check_group_invariants(buf, E, k):
+    ids = buf.topk_id.cpu().numpy()
+    T = ids.shape[0]
+    count = buf.count.cpu().numpy()
+    offset = buf.offset.cpu().numpy()
+    ss = buf.sorted_slot.cpu().numpy()
+    sr = buf.slot_row.cpu().numpy()
+    active = buf.active.cpu().numpy()
+    na = int(buf.n_active.item())
+    assert np.array_equal(count, np.bincount(ids.ravel(), minlength=E))
+    assert offset[0] == 0 and np.array_equal(np.diff(offset), count) and offset[E] == T * k
+    assert np.array_equal(np.sort(ss), np.arange(T * k))
+    assert np.array_equal(sr[ss], np.arange(T * k))
+    for e in np.nonzero(count)[0]:
+        seg = ss[offset[e]:offset[e + 1]]
+        assert np.all(np.diff(seg) > 0) and np.all(ids.ravel()[seg] == e)
+    act = [e for e in range(E) if count[e] > 0]
+    act.sort(key=lambda e: (-count[e], e))
+    assert na == len(act) and list(active[:na]) == act and np.all(active[na:] == -1)
+    for t in range(min(T, 64)):
+        assert len(set(ids[t].tolist())) == k  # distinct experts per token
+
+
+def _check_tokens(sp, L, ex_host, buf, tokens, x_all, t_offset=0):
+    k = sp["k"]
+    xb = x_all.cpu().view(torch.int16).numpy().view(np.uint16)
+    wr = L["w_router"].cpu().numpy()
+    bias = None if L["bias"] is None else L["bias"].cpu().numpy()
+    ref = oracle.layer_tokens(xb, wr, bias, ex_host, k, [t + t_offset for t in tokens])
+    g_ids = buf.topk_id.cpu().numpy()[tokens]
+    g_w = buf.topk_w.cpu().numpy()[tokens]
+    g_logits = buf.logits.cpu().numpy()[tokens]
+    assert np.max(np.abs(g_logits - ref["logits"])) <= LOGIT_TOL
+    exempt = check_routing(g_ids, g_w, ref["logits"], ref["topk_w"], k)
+    r_out = ref["out"].copy()
+    for i, ids in exempt.items():
+        r_out[i] = oracle_token_out(xb, ex_host, tokens[i] + t_offset, ids, ref["logits"][i])
+    g_out = buf.out.cpu().numpy()[tokens]
+    mr, ma = check_out(g_out, r_out)
+    print("tokens %s: max_rel %.3e mae %.3e near-ties %d" % (tokens, mr, ma, len(exempt)))
+
+
+def test_decode1_full():
+    """T=1 calls on pool tokens 0..3 (each call = one benchmark step)."""
+    sp, L, ex_host = _layer("decode1")
+    print("case decode1 T=1 H=7168 I=2048 E=256 k=8", flush=True)
+    for t in range(4):
+        x = L["x"][t:t + 1]
+        buf = _run(L, x, sp["k"])
+        _check_group_invariants(buf, sp["E"], sp["k"])
+        _check_tokens(sp, L, ex_host, buf, [0], L["x"], t_offset=t)
+
+
+def test_decode64_full():
+    sp, L, ex_host = _layer("decode64")
+    print("case decode64 T=64", flush=True)
+    buf = _run(L, L["x"], sp["k"])
+    _check_group_invariants(buf, sp["E"], sp["k"])
+    counts = buf.count.cpu().numpy()
+    ids = buf.topk_id.cpu().numpy()
+    busiest = int(np.argmax(counts))
+    t_busy = int(np.nonzero((ids == busiest).any(1))[0][0])  # a token of the busiest expert
+    _check_tokens(sp, L, ex_host, buf, sorted({0, 31, 63, t_busy}), L["x"])
+
+
+def test_verify128_full():
+    sp, L, ex_host = _layer("verify128")
+    print("case verify128 T=128 I=256 zipf", flush=True)
+    buf = _run(L, L["x"], sp["k"])
+    _check_group_invariants(buf, sp["E"], sp["k"])
+    counts = buf.count.cpu().numpy()
+    assert counts.max() > 16  # the Zipf bias makes some experts busy (matrix-core path)
+    ids = buf.topk_id.cpu().numpy()
+    hot = int(np.argmax(counts))
+    toks = sorted({0, 77, 127} | set(np.nonzero((ids == hot).any(1))[0][:3].tolist()))
+    _check_tokens(sp, L, ex_host, buf, toks, L["x"])
+
+
+def test_prefill16k_full():
+    sp, L, ex_host = _layer("prefill16k")
+    print("case prefill16k T=16384", flush=True)
+    buf = _run(L, L["x"], sp["k"])
+    _check_group_invariants(buf, sp["E"], sp["k"])
+    counts = buf.count.cpu().numpy()
+    assert counts.min() > 300 and counts.max() < 800
+    _check_tokens(sp, L, ex_host, buf, [0, 4097, 9999, 16383], L["x"])
