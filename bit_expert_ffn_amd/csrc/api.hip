@@ -23,7 +23,8 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   }
   L.ffn_x16 = 0;
   L.ffn_h16 = align_up((size_t)T * H * sizeof(_Float16), 256);
-  L.ffn_end = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
+  L.ffn_tiles = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
+  L.ffn_end = L.ffn_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
   size_t tot = L.route_end;
   if (L.group_end > tot) tot = L.group_end;
   if (L.ffn_end > tot) tot = L.ffn_end;
@@ -147,7 +148,9 @@ MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_exper
   a.y_f16 = y_dtype == MOE_F16;
   a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
   a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
-  return from_hip(moe::launch_ffn(a, (hipStream_t)stream));
+  int2* tiles = reinterpret_cast<int2*>((char*)ws_dev + L.ffn_tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + moe::gemm_max_tiles(T, k, w->E));
+  return from_hip(moe::launch_ffn(a, tiles, n_tiles, (hipStream_t)stream));
 }
 
 MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t* slot_row_dev,

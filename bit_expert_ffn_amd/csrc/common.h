@@ -36,6 +36,7 @@ struct WsLayout {
   size_t group_end;
   size_t ffn_x16;        // [T][H] f16
   size_t ffn_h16;        // [T*k][I] f16
+  size_t ffn_tiles;      // busy-expert tile list: [gemm_max_tiles] int2, then the count (int32)
   size_t ffn_end;
   size_t total;
 };
@@ -59,7 +60,11 @@ struct FfnArgs {
   _Float16* x16;  // workspace
   _Float16* h16;  // workspace
 };
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream_t s);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t* n_tiles,
+                           hipStream_t s);
+int gemm_rows_per_tile(int T);
+size_t gemm_max_tiles(int T, int k, int E);
 
 hipError_t launch_pack(const uint8_t* q_in, const uint8_t* s_in, int E, int N, int K,
                        uint8_t* q_out, uint8_t* s_out, hipStream_t s);

@@ -1,246 +1,31 @@
-// Expert FFN over NVFP4 weights: gate/up -> SwiGLU -> down for every routed row.
+// Expert FFN over NVFP4 weights, few-row experts, and the dispatch of the whole FFN call.
 //
 // Sources: per expert gate/up, SwiGLU, then down ("Optimizing Muse Spark Open on TPU v7 with
 // SGLang-TorchTPU", section 8, "The fused MoE kernel and the pair exchange"); packed 4-bit
 // weights are streamed and unpacked with their per-16 block scale in registers, never
-// dequantised to HBM; a grouped GEMM runs over the active experts only ("Optimizing Models to
-// Be Fast at Codegen", section 2 "Kernels optimized for latency or throughput"); a few-row
-// expert fits in the same row tile as a single token (Muse Spark page, section 6).
+// dequantised to HBM ("Optimizing Models to Be Fast at Codegen", section 2 "Kernels optimized
+// for latency or throughput"); experts are split by row count into a few-row path and a busy
+// path (Muse Spark page, section 5).
 //
-// Matrix-core mapping (gfx950, v_mfma_f32_16x16x32_f16, 64-lane wavefronts):
-//   one wavefront computes a 16 (rows) x 16 (features) tile.  K is walked in chunks of 128.
-//   The weights are tile-major (see pack.hip): for a 16-feature row tile and chunk c, lane
-//   l = 16*g + n gets feature n's 32 values K = [c*128 + g*32, +32) with one 16-byte load, and
-//   the wavefront's 64 loads are one contiguous 1 KB block (plus 128 contiguous scale bytes).
-//   Those 32 values feed four MFMAs (8 each).  The MFMA sums over its 32 k positions, so the
-//   order of K inside the chunk is free; the A operand (activations) is read with the same
-//   permutation: lane l = 16*g + m supplies row m's values [c*128 + g*32 + 8i, +8) to MFMA i.
-// Decode: v_cvt_scalef32_pk_f16_fp4 turns one byte (two e2m1 codes) into two exact f16
-//   values; the hardware uses only the exponent of its fp32 scale operand, so the e4m3 block
-//   scale (converted to f16 by v_cvt_scalef32_pk_f16_fp8) is applied with one v_pk_mul_f16.
-//   e2m1 * e4m3 needs at most 6 significant bits and lies in [2^-10, 2688], so the f16 weight
-//   is exact.  The fp32 tensor scale multiplies the fp32 accumulator once.
-// Activations: x (bf16) is converted once to f16 (exact for |x| in [2^-17, 65504]); h is
-//   stored as f16.
+// Dispatch: every expert has at most T rows (a token's k experts are distinct).  The host picks
+// R in {1, 2, 4} from T; experts with <= R rows run the VALU kernels below, the others the
+// matrix-core grouped GEMM (gemm.hip).  Both read the tile-major weight layout (pack.hip): for a
+// 16-feature row tile and a 128-column chunk, lane l = 16*g + n of a wavefront loads feature
+// n's 32 values K = [c*128 + g*32, +32) (16 bytes) and their two e4m3 scale bytes; the
+// wavefront's 64 loads are one contiguous 1 KB block.
+// Decode: v_cvt_scalef32_pk_{bf16,f16}_fp4 turns one byte (two e2m1 codes) into two exact
+// 16-bit values (the hardware uses only the exponent of its fp32 scale operand, so it is given
+// 1.0); the e4m3 block scale multiplies each 16-value block sum in fp32; the fp32 tensor scale
+// multiplies the final sum once.
+// Activations: x is dotted as bf16 (exact); h is stored as f16 (the down projection's input).
 #include "common.h"
 
 namespace moe {
 
-constexpr int kChunk = 128;         // K values per chunk
-constexpr int kTileM = 16;          // rows per tile
-
-__device__ inline f16x8 decode8(uint32_t q, f16x2 s) {
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * s;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * s;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * s;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * s;
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// acc += A(16 x 128 chunk) * B(128 chunk x 16) for one chunk: 4 MFMAs.
-__device__ inline f32x4 mma_chunk(f32x4 acc, const f16x8 a[4], uint4 q, uint32_t sbytes) {
-  const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbytes, 1.0f, false);
-  const f16x2 s0 = {sc[0], sc[0]};
-  const f16x2 s1 = {sc[1], sc[1]};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], decode8(q.x, s0), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], decode8(q.y, s0), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], decode8(q.z, s1), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], decode8(q.w, s1), acc, 0, 0, 0);
-  return acc;
-}
-
-// A operand of one chunk for this lane (64 contiguous bytes).  Lanes whose tile row is past the
-// expert's last row load a valid row instead: an MFMA output row depends only on the same A
-// row, and those output rows are never stored, so no lane needs a branch around its loads.
-__device__ inline void load_a(f16x8 a[4], const _Float16* p) {
-  const uint4* v = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(f16x8, v[i]);
-}
+constexpr int kChunk = 128;  // K values per chunk (one tile-major column block)
 
 __device__ inline uint32_t load_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
-}
-
-// x [T][H] bf16 -> f16, 8 values per thread.
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x,
-                                                       _Float16* __restrict__ x16, size_t n8) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const uint4 v = reinterpret_cast<const uint4*>(x)[i];
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  f16x8 o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    o[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
-    o[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xffff0000u);
-  }
-  reinterpret_cast<f16x8*>(x16)[i] = o;
-}
-
-// Gate/up + SwiGLU.  Grid: (I / 16, max active experts).  Block: KSPLIT wavefronts that split
-// the K chunks of one 16-feature tile of gate and of up (same features, so h = silu(g) * u is
-// formed in registers).  Each wavefront loads kBatch chunks (codes, scales, activations)
-// before decoding them, so several KB per wavefront are in flight.  The split partial sums are
-// added in LDS in wavefront order.  The block walks the expert's rows 16 at a time.
-constexpr int kBatch = 4;
-
-template <int KSPLIT>
-__global__ __launch_bounds__(64 * KSPLIT) void ffn_gateup_tile_kernel(
-    const _Float16* __restrict__ x16, const uint8_t* __restrict__ gq,
-    const uint8_t* __restrict__ uq, const uint8_t* __restrict__ gs,
-    const uint8_t* __restrict__ us, const float* __restrict__ ts,
-    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16,
-    int min_rows) {
-  __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][2][64];
-  const int slot = blockIdx.y;
-  if (slot >= *n_active) return;
-  const int e = active[slot];
-  const int rows = count[e];
-  if (rows < min_rows) return;  // a few-row expert: the VALU path takes it
-  const int base = offset[e];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int f0 = blockIdx.x * 16;
-  const int nchunk = H / kChunk;
-  // tile-major weights: row tile blockIdx.x of expert e, chunk c at tile index (rt*nchunk + c)
-  const size_t tile0 = (size_t)blockIdx.x * nchunk;
-  const uint8_t* gqp = gq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
-  const uint8_t* uqp = uq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
-  const uint8_t* gsp = gs + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
-  const uint8_t* usp = us + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
-  const int per = (nchunk + KSPLIT - 1) / KSPLIT;
-  const int cb = min(nchunk, wv * per), ce = min(nchunk, cb + per);
-  for (int m0 = 0; m0 < rows; m0 += kTileM) {
-    const int ra = min(m0 + n, rows - 1);  // A row of this lane (m = lane & 15), clamped
-    const int tok = sorted_slot[base + ra] / k;
-    const _Float16* ap = x16 + (size_t)tok * H + g * 32;
-    f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    for (int c = cb; c < ce; c += kBatch) {
-      uint4 qg[kBatch], qu[kBatch];
-      uint32_t sg[kBatch], su[kBatch];
-      f16x8 a[kBatch][4];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (c + u < ce) {
-          const int cc = c + u;
-          qg[u] = *reinterpret_cast<const uint4*>(gqp + cc * 1024);
-          qu[u] = *reinterpret_cast<const uint4*>(uqp + cc * 1024);
-          sg[u] = load_u16(gsp + cc * 128);
-          su[u] = load_u16(usp + cc * 128);
-          load_a(a[u], ap + cc * kChunk);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (c + u < ce) {
-          accg = mma_chunk(accg, a[u], qg[u], sg[u]);
-          accu = mma_chunk(accu, a[u], qu[u], su[u]);
-        }
-      }
-    }
-    if (KSPLIT > 1) {
-      red[wv][0][lane] = accg;
-      red[wv][1][lane] = accu;
-      __syncthreads();
-      if (wv == 0) {
-#pragma unroll
-        for (int w = 1; w < KSPLIT; ++w) {
-          accg += red[w][0][lane];
-          accu += red[w][1][lane];
-        }
-      }
-    }
-    if (wv == 0) {
-      const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + g * 4 + r;
-        if (m < rows) {
-          const float gv = accg[r] * tsg, uv = accu[r] * tsu;
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          h16[(size_t)(base + m) * I + f0 + n] = (_Float16)hv;
-        }
-      }
-    }
-    if (KSPLIT > 1) __syncthreads();
-  }
-}
-
-// Down projection.  Grid: (H / 16, max active experts).  A = h rows (grouped order, f16).
-template <int KSPLIT, bool Y_F16>
-__global__ __launch_bounds__(64 * KSPLIT) void ffn_down_tile_kernel(
-    const _Float16* __restrict__ h16, const uint8_t* __restrict__ dq,
-    const uint8_t* __restrict__ dsc, const float* __restrict__ ts,
-    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int H, int I,
-    void* __restrict__ y, int min_rows) {
-  __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT : 1][64];
-  const int slot = blockIdx.y;
-  if (slot >= *n_active) return;
-  const int e = active[slot];
-  const int rows = count[e];
-  if (rows < min_rows) return;
-  const int base = offset[e];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int f0 = blockIdx.x * 16;
-  const int nchunk = I / kChunk;
-  const size_t tile0 = (size_t)blockIdx.x * nchunk;
-  const uint8_t* qp = dq + (size_t)e * ((size_t)H * I / 2) + (tile0 * 64 + lane) * 16;
-  const uint8_t* sp = dsc + (size_t)e * ((size_t)H * I / 16) + (tile0 * 64 + lane) * 2;
-  const int per = (nchunk + KSPLIT - 1) / KSPLIT;
-  const int cb = min(nchunk, wv * per), ce = min(nchunk, cb + per);
-  for (int m0 = 0; m0 < rows; m0 += kTileM) {
-    const int ra = min(m0 + n, rows - 1);  // clamped, as in the gate/up kernel
-    const _Float16* ap = h16 + (size_t)(base + ra) * I + g * 32;
-    f32x4 acc = {0, 0, 0, 0};
-    for (int c = cb; c < ce; c += kBatch) {
-      uint4 q[kBatch];
-      uint32_t sc[kBatch];
-      f16x8 a[kBatch][4];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (c + u < ce) {
-          const int cc = c + u;
-          q[u] = *reinterpret_cast<const uint4*>(qp + cc * 1024);
-          sc[u] = load_u16(sp + cc * 128);
-          load_a(a[u], ap + cc * kChunk);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (c + u < ce) acc = mma_chunk(acc, a[u], q[u], sc[u]);
-    }
-    if (KSPLIT > 1) {
-      red[wv][lane] = acc;
-      __syncthreads();
-      if (wv == 0) {
-#pragma unroll
-        for (int w = 1; w < KSPLIT; ++w) acc += red[w][lane];
-      }
-    }
-    if (wv == 0) {
-      const float tsd = ts[e * 3 + 2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + g * 4 + r;
-        if (m < rows) {
-          const float v = acc[r] * tsd;
-          const size_t o = (size_t)(base + m) * H + f0 + n;
-          if (Y_F16)
-            reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
-          else
-            reinterpret_cast<float*>(y)[o] = v;
-        }
-      }
-    }
-    if (KSPLIT > 1) __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -519,18 +304,6 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
   }
 }
 
-static int pick_ksplit(int blocks, int nchunk) {
-  int ks = (6144 + blocks - 1) / blocks;
-  if (ks > 4) ks = 4;
-  if (ks > nchunk) ks = nchunk;
-  if (ks >= 4) return 4;
-  if (ks >= 2) return 2;
-  return 1;
-}
-
-// Rows per expert handled by the few-row path for a given token count (0: none).  An expert
-// has at most T rows (a token's k experts are distinct).  The LDS staging of the activation
-// rows bounds R * K * 2 bytes to 64 KB.
 // K slices per 16-feature tile in the few-row kernels: enough wavefronts (and bytes in flight)
 // to cover the HBM latency when there are few tiles.
 static int few_ksplit(int tiles, int nchunk) {
@@ -546,14 +319,10 @@ static int few_rows(int T, int H, int I) {
   return R;
 }
 
-hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream_t s) {
   const int maxe = a.E < a.T * a.k ? a.E : a.T * a.k;
   const int R = few_rows(a.T, a.H, a.I);
   const bool heavy = a.T > R;  // some expert may have more than R rows
-  if (heavy) {
-    const size_t n8 = (size_t)a.T * a.H / 8;
-    x_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(a.x, a.x16, n8);
-  }
   // gate/up + SwiGLU
   if (R > 0) {
     const int ks = few_ksplit(maxe * (a.I / 16), a.H / kChunk);
@@ -575,19 +344,6 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     else MOE_FEW_GU_R(4);
 #undef MOE_FEW_GU_R
 #undef MOE_FEW_GU
-  }
-  if (heavy) {
-    const int ksg = pick_ksplit(maxe * (a.I / 16), a.H / kChunk);
-    const dim3 gg(a.I / 16, maxe);
-#define MOE_GATEUP(KS_)                                                                   \
-  ffn_gateup_tile_kernel<KS_><<<gg, 64 * KS_, 0, s>>>(a.x16, a.gq, a.uq, a.gs, a.us, a.ts, \
-                                                      a.count, a.offset, a.sorted_slot,    \
-                                                      a.active, a.n_active, a.k, a.H, a.I, \
-                                                      a.h16, R + 1)
-    if (ksg == 4) MOE_GATEUP(4);
-    else if (ksg == 2) MOE_GATEUP(2);
-    else MOE_GATEUP(1);
-#undef MOE_GATEUP
   }
   // down
   if (R > 0) {
@@ -616,24 +372,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
 #undef MOE_FEW_D_R
 #undef MOE_FEW_D
   }
-  if (heavy) {
-    const int ksd = pick_ksplit(maxe * (a.H / 16), a.I / kChunk);
-    const dim3 gd(a.H / 16, maxe);
-#define MOE_DOWN(KS_, F16_)                                                                    \
-  ffn_down_tile_kernel<KS_, F16_><<<gd, 64 * KS_, 0, s>>>(a.h16, a.dq, a.ds, a.ts, a.count,   \
-                                                          a.offset, a.active, a.n_active, a.H, \
-                                                          a.I, a.y, R + 1)
-    if (a.y_f16) {
-      if (ksd == 4) MOE_DOWN(4, true);
-      else if (ksd == 2) MOE_DOWN(2, true);
-      else MOE_DOWN(1, true);
-    } else {
-      if (ksd == 4) MOE_DOWN(4, false);
-      else if (ksd == 2) MOE_DOWN(2, false);
-      else MOE_DOWN(1, false);
-    }
-#undef MOE_DOWN
-  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (heavy) return launch_ffn_gemm(a, R + 1, tiles, n_tiles, s);
   return hipGetLastError();
 }
 
