@@ -74,4 +74,14 @@ hipError_t launch_combine(const void* y, int y_f16, const int32_t* slot_row, con
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases global memory, which
+// makes every wavefront wait for all of its outstanding global loads (vmcnt(0)) before the
+// barrier; a kernel whose global loads only feed registers (prefetch for later stages) keeps
+// them in flight across this barrier instead.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace moe

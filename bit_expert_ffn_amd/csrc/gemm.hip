@@ -12,24 +12,15 @@
 // min_rows rows: (expert, first row).  grid.y runs over a host-side bound of that list; blocks
 // past its end return.  Nothing is read back by the host.
 //
-// Block: 256 threads = 2 x 2 wavefronts, MT rows x 128 weight rows, K in stages of 64.
-//   gate/up: the 128 weight rows are 64 gate rows and the same 64 up rows, so each wavefront
-//            holds gate and up accumulators of the same 32 features and forms h = silu(g) * u
-//            in registers (h stored as f16);
-//   down:    the 128 weight rows are 128 output features.
-// Per stage every thread loads its share of the activation tile (16-byte pieces of gathered
-// rows) and 16 bytes of packed codes + 2 scale bytes of one weight tile row, decodes the 32
-// weights (v_cvt_scalef32_pk_f16_fp4, then the e4m3 block scale with v_pk_mul_f16, exact in
-// f16) and writes both tiles to LDS (rows padded to 144 bytes).  LDS is double buffered and the
-// global loads run two stages ahead in registers.  Each wavefront then issues WM x 2 MFMAs
-// (v_mfma_f32_32x32x16_f16, fp32 accumulate) per 16 columns of K.
+// Arithmetic: activations (x or h) and decoded weights enter v_mfma_f32_32x32x16_f16 as f16;
+// e2m1 * e4m3 is exact in f16 (at most 6 significant bits, magnitude in [2^-10, 2688]); the
+// fp32 tensor scales multiply the fp32 accumulators in the epilogue.
 #include "common.h"
 
 namespace moe {
 
 constexpr int gK = 64;       // K per pipeline stage
 constexpr int gLD = gK + 8;  // padded LDS row, in halves
-constexpr int gBR = 128;     // weight rows per block
 constexpr int kXcds = 8;     // MI355X: 8 accelerator dies (XCDs), workgroups dealt round-robin
 constexpr int kGroup = 4;    // consecutive row tiles whose blocks are ordered together
 
@@ -94,8 +85,22 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     ffn_plan(count, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
+// Block: 256 threads = 2 x 2 wavefronts; MT = 64 * WM rows x 256 weight rows; K in stages of
+// 64.  Wavefront (wm, wn) computes rows wm * 32 * WM .. (WM tiles of 32) against 4 weight tiles
+// of 32 rows:
+//   gate/up: gate rows f0 + 64 wn + {0, 32} and the same up rows -> 64 features per wavefront,
+//            128 per block, h = silu(g) * u in the epilogue;
+//   down:    rows n0 + 128 wn + {0, 32, 64, 96} -> 256 output features per block.
+// Activations go through LDS (double buffered, rows padded to 144 bytes).  Weights do not: each
+// lane loads, per stage and per weight tile, the 16 packed bytes (32 codes) of weight row
+// l % 32 and K-group 2 (st % 2) + l / 32 of the stage's 128-column chunk, plus two scale bytes,
+// and decodes one code dword right before each of the stage's four 16-K MFMA steps.  The MFMA
+// sums over its 16 k positions, so K may be permuted: step i takes codes 8i..8i+7 of the
+// lane's group, and the activation operand is read from LDS columns 32 (l / 32) + 8i of the
+// stage (same permutation).  Global loads of activations and packed weights run ahead in two
+// register sets (even / odd stages).
 template <bool GATEUP, int WM, bool Y_F16>
-__global__ __launch_bounds__(256) void ffn_gemm_kernel(
+__global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
@@ -104,14 +109,15 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out) {
   constexpr int MT = 64 * WM;
   constexpr int NA = 2 * WM;  // 16-byte activation pieces per thread per stage
+  constexpr int NT = 4;       // weight tiles of 32 rows per wavefront
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native vector: stays in VGPRs
   __shared__ __attribute__((aligned(16))) _Float16 As[2][MT][gLD];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][gBR][gLD];
   // Block order.  Workgroups go round-robin to the 8 XCDs, each with its own L2; renumber so
   // that every XCD gets one contiguous range of the logical order, and in that order take
   // groups of kGroup consecutive row tiles (about one expert), then the weight blocks, then the
   // tiles of the group.  The blocks resident on one XCD then share a few activation tiles and
   // a few weight slices.
-  const int NB = gridDim.x;  // weight blocks (feature blocks)
+  const int NB = gridDim.x;  // weight blocks
   const int ntl = *n_tiles;
   const int total = NB * ntl;
   const int bid = blockIdx.x + NB * blockIdx.y;
@@ -139,47 +145,73 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(
   const int nchunk = K / 128;
   const int nstage = K / gK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
 
   // activation rows of this thread's pieces (rows past the expert's end repeat its last row:
-  // their outputs are never stored).  Named variables, not arrays, so that they stay in
-  // registers.
-  auto arow_of = [&](int i) __attribute__((always_inline)) {
+  // their outputs are never stored).  Offsets are 32-bit element offsets from a uniform base
+  // (x and h are far below 2^32 elements), which keeps the per-lane state small.
+  auto aoff_of = [&](int i) __attribute__((always_inline)) {
     const int s = tid + 256 * i;
     const int r = min(m0 + (s >> 3), rows - 1);
-    const size_t src = GATEUP ? (size_t)(sorted_slot[base + r] / k) * H : (size_t)(base + r) * I;
-    return xa + src + (s & 7) * 8;
+    const uint32_t src = GATEUP ? (uint32_t)(sorted_slot[base + r] / k) * (uint32_t)H
+                                : (uint32_t)(base + r) * (uint32_t)I;
+    return src + (uint32_t)(s & 7) * 8;
   };
-  const _Float16* arow0 = arow_of(0);
-  const _Float16* arow1 = arow_of(1);
-  const _Float16* arow2 = NA > 2 ? arow_of(2) : arow0;
-  const _Float16* arow3 = NA > 2 ? arow_of(3) : arow0;
-  // weight tile row of this thread: 8 tiles of 16 rows, 32 threads per tile
-  const int bt = tid >> 5, sub = tid & 31;
-  const int rt = GATEUP ? fb * 4 + (bt & 3) : fb * 8 + bt;
-  const uint8_t* qsel = (GATEUP && bt >= 4) ? qm1 : qm0;
-  const uint8_t* ssel = (GATEUP && bt >= 4) ? sm1 : sm0;
-  const uint8_t* qb = qsel + (size_t)e * ((size_t)N * K / 2) + (size_t)rt * nchunk * 1024;
-  const uint8_t* sb = ssel + (size_t)e * ((size_t)N * K / 16) + (size_t)rt * nchunk * 128;
+  const uint32_t aoff0 = aoff_of(0);
+  const uint32_t aoff1 = aoff_of(1);
+  const uint32_t aoff2 = NA > 2 ? aoff_of(2) : aoff0;
+  const uint32_t aoff3 = NA > 2 ? aoff_of(3) : aoff0;
 
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native vector: stays in VGPRs
+  // weight rows of this lane in its 4 weight tiles; rows past N (only possible in the last
+  // block of down when H % 256 != 0) re-read row N - 1 and are never stored.  Byte offsets
+  // within the expert's matrix (< 2^32) from uniform bases.
+  const int r32 = lane & 31, hgrp = lane >> 5;
+  const uint8_t* qb0 = qm0 + (size_t)e * ((size_t)N * K / 2);
+  const uint8_t* sb0 = sm0 + (size_t)e * ((size_t)N * K / 16);
+  const uint8_t* qb1 = GATEUP ? qm1 + (size_t)e * ((size_t)N * K / 2) : qb0;
+  const uint8_t* sb1 = GATEUP ? sm1 + (size_t)e * ((size_t)N * K / 16) : sb0;
+  uint32_t qoff[NT], soff[NT];
+  int feat[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = GATEUP ? fb * 128 + wn * 64 + (t & 1) * 32 + r32
+                           : fb * 256 + wn * 128 + t * 32 + r32;
+    feat[t] = row;
+    const int rc = min(row, N - 1);
+    const uint32_t tile0 = (uint32_t)(rc >> 4) * (uint32_t)nchunk;
+    qoff[t] = tile0 * 1024u + (uint32_t)(rc & 15) * 16u + (uint32_t)hgrp * 256u;
+    soff[t] = tile0 * 128u + (uint32_t)(rc & 15) * 2u + (uint32_t)hgrp * 32u;
+  }
+  auto qbase = [&](int t) __attribute__((always_inline)) { return (GATEUP && t >= 2) ? qb1 : qb0; };
+  auto sbase = [&](int t) __attribute__((always_inline)) { return (GATEUP && t >= 2) ? sb1 : sb0; };
+
   struct Stage {
     u32x4 a0, a1, a2, a3;
-    u32x4 b;
-    uint32_t s;
+    u32x4 q0, q1, q2, q3;
+    uint32_t s0, s1, s2, s3;
   };
   auto load = [&](Stage& r, int st) __attribute__((always_inline)) {
-    const int k0 = st * gK;
-    r.a0 = *reinterpret_cast<const u32x4*>(arow0 + k0);
-    r.a1 = *reinterpret_cast<const u32x4*>(arow1 + k0);
+    const uint32_t k0 = (uint32_t)st * gK;
+    r.a0 = *reinterpret_cast<const u32x4*>(xa + (aoff0 + k0));
+    r.a1 = *reinterpret_cast<const u32x4*>(xa + (aoff1 + k0));
     if (NA > 2) {
-      r.a2 = *reinterpret_cast<const u32x4*>(arow2 + k0);
-      r.a3 = *reinterpret_cast<const u32x4*>(arow3 + k0);
+      r.a2 = *reinterpret_cast<const u32x4*>(xa + (aoff2 + k0));
+      r.a3 = *reinterpret_cast<const u32x4*>(xa + (aoff3 + k0));
     }
-    const int l = (st & 1) * 32 + sub;  // tile lane of this stage's 64-column half
-    r.b = *reinterpret_cast<const u32x4*>(qb + ((size_t)(st >> 1) * 64 + l) * 16);
-    r.s = *reinterpret_cast<const uint16_t*>(sb + ((size_t)(st >> 1) * 64 + l) * 2);
+    // tile-lane of this lane's K-group in the stage's chunk: 16 * g + row % 16, where
+    // g = 2 (st % 2) + lane / 32 (the lane / 32 part is already in qoff / soff)
+    const uint32_t cq = (uint32_t)(st >> 1) * 1024u + (uint32_t)(st & 1) * 512u;
+    const uint32_t cs = (uint32_t)(st >> 1) * 128u + (uint32_t)(st & 1) * 64u;
+    r.q0 = *reinterpret_cast<const u32x4*>(qbase(0) + (qoff[0] + cq));
+    r.q1 = *reinterpret_cast<const u32x4*>(qbase(1) + (qoff[1] + cq));
+    r.q2 = *reinterpret_cast<const u32x4*>(qbase(2) + (qoff[2] + cq));
+    r.q3 = *reinterpret_cast<const u32x4*>(qbase(3) + (qoff[3] + cq));
+    r.s0 = *reinterpret_cast<const uint16_t*>(sbase(0) + (soff[0] + cs));
+    r.s1 = *reinterpret_cast<const uint16_t*>(sbase(1) + (soff[1] + cs));
+    r.s2 = *reinterpret_cast<const uint16_t*>(sbase(2) + (soff[2] + cs));
+    r.s3 = *reinterpret_cast<const uint16_t*>(sbase(3) + (soff[3] + cs));
   };
-  auto store = [&](const Stage& r, int buf) __attribute__((always_inline)) {
+  auto store_a = [&](const Stage& r, int buf) __attribute__((always_inline)) {
     // piece i of this thread: s = tid + 256 * i -> row s >> 3, 16-byte column s & 7
     const int c8 = (tid & 7) * 8;
     *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3)][c8]) = r.a0;
@@ -188,79 +220,77 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(
       *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 64][c8]) = r.a2;
       *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 96][c8]) = r.a3;
     }
-    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s, 1.0f, false);
-    const f16x2 s0 = {sc[0], sc[0]};
-    const f16x2 s1 = {sc[1], sc[1]};
-    _Float16* dst = &Bs[buf][bt * 16 + (sub & 15)][(sub >> 4) * 32];
-    *reinterpret_cast<f16x8*>(dst + 0) = gdecode8(r.b.x, s0);
-    *reinterpret_cast<f16x8*>(dst + 8) = gdecode8(r.b.y, s0);
-    *reinterpret_cast<f16x8*>(dst + 16) = gdecode8(r.b.z, s1);
-    *reinterpret_cast<f16x8*>(dst + 24) = gdecode8(r.b.w, s1);
   };
 
-  const int wm = w & 1, wn = w >> 1;
-  f32x16 acc[WM][2];
+  f32x16 acc[WM][NT];
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+      for (int v = 0; v < 16; ++v) acc[i][t][v] = 0.f;
+  auto bfrag = [&](u32x4 q, uint32_t sbytes, int step) __attribute__((always_inline)) {
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbytes, 1.0f, false);
+    const f16x2 sv = step < 2 ? f16x2{sc[0], sc[0]} : f16x2{sc[1], sc[1]};
+    return gdecode8(q[step], sv);
+  };
+  auto compute = [&](const Stage& r, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < gK; kk += 16) {
-      f16x8 a[WM], b[2];
+    for (int step = 0; step < 4; ++step) {
+      f16x8 a[WM];
 #pragma unroll
       for (int i = 0; i < WM; ++i)
         a[i] = *reinterpret_cast<const f16x8*>(
-            &As[buf][wm * 32 * WM + i * 32 + (lane & 31)][kk + (lane >> 5) * 8]);
+            &As[buf][wm * 32 * WM + i * 32 + r32][hgrp * 32 + step * 8]);
+      const f16x8 b0 = bfrag(r.q0, r.s0, step);
+      const f16x8 b1 = bfrag(r.q1, r.s1, step);
+      const f16x8 b2 = bfrag(r.q2, r.s2, step);
+      const f16x8 b3 = bfrag(r.q3, r.s3, step);
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn) {
-        const int brow = GATEUP ? jn * 64 + wn * 32 : wn * 64 + jn * 32;
-        b[jn] = *reinterpret_cast<const f16x8*>(&Bs[buf][brow + (lane & 31)][kk + (lane >> 5) * 8]);
+      for (int i = 0; i < WM; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b1, acc[i][1], 0, 0, 0);
+        acc[i][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b2, acc[i][2], 0, 0, 0);
+        acc[i][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b3, acc[i][3], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-          acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
     }
   };
 
-  // pipeline: LDS double buffer; global loads two stages ahead (register sets r0 / r1 hold
-  // the even / odd stages).  nstage = K / 64 is even (K is a multiple of 128), so the loop body
-  // has no conditions; the two loads past the last stage re-read it (clamped) and are unused.
+  // pipeline: nstage = K / 64 is even (K is a multiple of 128), so the loop body has no
+  // conditions; the loads past the last stage re-read it (clamped) and are unused.
   Stage r0, r1;
   load(r0, 0);
   load(r1, 1);
-  store(r0, 0);
-  load(r0, min(2, nstage - 1));
-  __syncthreads();
+  store_a(r0, 0);
+  lds_barrier();
   for (int st = 0; st < nstage; st += 2) {
-    compute(0);
-    store(r1, 1);
+    compute(r0, 0);
+    store_a(r1, 1);
+    load(r0, min(st + 2, nstage - 1));
+    lds_barrier();
+    compute(r1, 1);
+    store_a(r0, 0);
     load(r1, min(st + 3, nstage - 1));
-    __syncthreads();
-    compute(1);
-    store(r0, 0);
-    load(r0, min(st + 4, nstage - 1));
-    __syncthreads();
+    lds_barrier();
   }
 
   // epilogue; accumulator element v of a 32x32 tile: row (v/4)*8 + (lane/32)*4 + v%4, col lane%32
-  const int rm = lane >> 5, cn = lane & 31;
+  const int rm = hgrp;
   if (GATEUP) {
-    const int f = fb * 64 + wn * 32 + cn;
     const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
     _Float16* h16 = reinterpret_cast<_Float16*>(out);
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 32 * WM + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
-        if (m < rows) {
-          const float gv = acc[i][0][v] * tsg, uv = acc[i][1][v] * tsu;
-          h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+      for (int t = 0; t < 2; ++t) {
+        const int f = feat[t];  // gate tile t and up tile t + 2 hold the same features
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 32 * WM + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
+          if (m < rows) {
+            const float gv = acc[i][t][v] * tsg, uv = acc[i][t + 2][v] * tsu;
+            h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+          }
         }
       }
   } else {
@@ -268,13 +298,14 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn) {
-        const int f = fb * 128 + wn * 64 + jn * 32 + cn;
+      for (int t = 0; t < NT; ++t) {
+        const int f = feat[t];
+        if (f >= N) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = m0 + wm * 32 * WM + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
           if (m < rows) {
-            const float yv = acc[i][jn][v] * tsd;
+            const float yv = acc[i][t][v] * tsd;
             const size_t o = (size_t)(base + m) * H + f;
             if (Y_F16)
               reinterpret_cast<_Float16*>(out)[o] = (_Float16)yv;
@@ -302,7 +333,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
   const size_t n8 = (size_t)a.T * a.H / 8;
   x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
       a.x, a.x16, n8, a.count, a.active, a.n_active, MT, min_rows, tiles, max_tiles, n_tiles);
-  const dim3 gg(a.I / 64, max_tiles), gd(a.H / 128, max_tiles);
+  const dim3 gg(a.I / 128, max_tiles), gd((a.H + 255) / 256, max_tiles);
 #define MOE_GEMM(GU_, WM_, F16_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
   ffn_gemm_kernel<GU_, WM_, F16_><<<GRID_, 256, 0, s>>>(XA_, Q0_, S0_, Q1_, S1_, a.ts,          \
                                                         a.count, a.offset, a.sorted_slot,       \
