@@ -70,7 +70,7 @@ def main():
     xs = layer["x"]
     wr, bias = layer["w_router"], layer["bias"]
     ex = moe.pack_experts(layer["experts"])  # tile-major copy (load-time conversion)
-    buf = moe.LayerBuffers(T, H, I, E, k, device=dev, y_dtype=torch.float32, logits=False)
+    buf = moe.LayerBuffers(T, H, I, E, k, device=dev, y_dtype=torch.float16, logits=False)
     torch.cuda.synchronize()
 
     def x_of(i):
@@ -121,7 +121,7 @@ def main():
     ms_step = elapsed * 1e3 / steps
     tok_s = T * steps / elapsed
     w_bytes = nd * expert_bytes(H, I)
-    ffn_bytes = w_bytes + T * H * 2 + T * k * H * 4          # weights + x + y
+    ffn_bytes = w_bytes + T * H * 2 + T * k * H * 2          # weights + x + y (f16)
     layer_bytes = ffn_bytes + H * E * 4 + T * H * 4          # + router weights + out
     flops = 6.0 * T * k * H * I
     if big:

@@ -13,7 +13,9 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   WsLayout L;
   const RoutePlan p = route_plan(T, H, E);
   L.route_partial = 0;
-  L.route_end = align_up((size_t)p.KS * T * E * sizeof(float), 256);
+  L.route_wsplit = align_up((size_t)p.KS * T * E * sizeof(float), 256);
+  L.route_end = L.route_wsplit;
+  if (p.mfma) L.route_end += align_up((size_t)3 * E * H * sizeof(uint16_t), 256);
   const size_t n = (size_t)T * k;
   L.group_whist = 0;
   L.group_end = 0;
@@ -85,8 +87,9 @@ MOE_API moe_status moe_route(const void* x_dev, const float* w_router_dev, const
   const moe::WsLayout L = moe::ws_layout(T, H, 128, E, k);
   if (ws_bytes < L.route_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   float* partial = reinterpret_cast<float*>((char*)ws_dev + L.route_partial);
+  uint16_t* wsplit = reinterpret_cast<uint16_t*>((char*)ws_dev + L.route_wsplit);
   return from_hip(moe::launch_route((const uint16_t*)x_dev, w_router_dev, bias_dev, T, H, E, k,
-                                    logits_dev, topk_id_dev, topk_w_dev, partial,
+                                    logits_dev, topk_id_dev, topk_w_dev, partial, wsplit,
                                     (hipStream_t)stream));
 }
 

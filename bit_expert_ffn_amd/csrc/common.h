@@ -21,16 +21,21 @@ constexpr int kGroupChunk = 16384;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Router launch plan: TT tokens per block (RG wavefronts), the hidden dimension split into KS
-// slices of kc rows, `tiles` token tiles.
+// slices of kc rows, `tiles` token tiles.  mfma: the matrix-core router (many tokens), which
+// needs the router weights split into three bf16 planes in the workspace.
 struct RoutePlan {
   int TT, RG, KS, kc, tiles;
+  bool mfma;
 };
+// fewest tokens for which the router runs on the matrix cores
+constexpr int kRouteMfmaMinT = 512;
 
 RoutePlan route_plan(int T, int H, int E);
 
 // Byte offsets of every call's scratch inside the caller's workspace.
 struct WsLayout {
   size_t route_partial;  // [KS][T][E] fp32
+  size_t route_wsplit;   // [3][E][H] bf16 (matrix-core router only)
   size_t route_end;
   size_t group_whist;    // [nblk*16][E] int32 (three-pass grouping only)
   size_t group_end;
@@ -44,7 +49,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k);
 
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                         int E, int k, float* logits, int32_t* topk_id, float* topk_w,
-                        float* partial, hipStream_t s);
+                        float* partial, uint16_t* wsplit, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* count,
                         int32_t* offset, int32_t* sorted_slot, int32_t* slot_row,
                         int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s);

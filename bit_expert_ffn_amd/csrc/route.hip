@@ -17,6 +17,15 @@
 //       are the softmax over the selected logits.
 // The kernel boundary between the two makes the partials visible without device-scope
 // fences inside a kernel.
+//
+// Many tokens (T >= kRouteMfmaMinT): the slices come from the matrix cores instead.
+//   router_split_kernel   writes each fp32 router weight as the exact sum of three bf16 values
+//       (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid), transposed to [3][E][H] so that
+//       8 consecutive hidden positions of one expert are 16 contiguous bytes.
+//   router_mfma_kernel    block = 128 tokens x 256 experts (4 wavefronts of 64 experts) over one
+//       slice of the hidden dimension; logits += x * hi + x * mid + x * lo on
+//       v_mfma_f32_32x32x16_bf16.  x is bf16, so every product is exact in fp32 and the result
+//       differs from the fp32 definition only in the order of the fp32 additions.
 #include "common.h"
 
 namespace moe {
@@ -26,6 +35,22 @@ constexpr int kRows = 16;  // router-weight rows per wavefront per batch of load
 RoutePlan route_plan(int T, int H, int E) {
   (void)E;
   RoutePlan p;
+  if (T >= kRouteMfmaMinT) {
+    // matrix-core router: 128-token tiles; split the hidden dimension until there are at least
+    // 512 blocks (two per CU), in slices that are multiples of 128
+    p.mfma = true;
+    p.TT = 128;
+    p.RG = 4;
+    p.tiles = (T + 127) / 128;
+    const int ks = (512 + p.tiles - 1) / p.tiles;
+    int kc = (H + ks - 1) / ks;
+    kc = (kc + 127) / 128 * 128;
+    if (kc > H) kc = H;
+    p.kc = kc;
+    p.KS = (H + kc - 1) / kc;
+    return p;
+  }
+  p.mfma = false;
   p.TT = T <= 1 ? 1 : T <= 4 ? 4 : T <= 64 ? 8 : 16;
   p.RG = p.TT <= 4 ? 8 : 4;
   const int tiles = (T + p.TT - 1) / p.TT;
@@ -121,6 +146,138 @@ __global__ __launch_bounds__(RG * 64) void router_slices_kernel(
   }
 }
 
+// bf16 nearest-even of a finite float (NaN stays NaN)
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// wr [H][E] fp32 -> wsplit [3][E][H] bf16 with w = hi + mid + lo exactly: hi keeps the leading
+// 8 significant bits (rounded), the residual w - hi is exact in fp32 and has at most 16
+// significant bits, mid keeps 8 of them and the remaining w - hi - mid fits in lo.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int H,
+                                                           int E, uint16_t* __restrict__ wsplit) {
+  __shared__ float tile[64][65];
+  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int hh = i >> 6, ee = i & 63;
+    float v = 0.f;
+    if (h0 + hh < H && e0 + ee < E) v = wr[(size_t)(h0 + hh) * E + e0 + ee];
+    tile[hh][ee] = v;
+  }
+  __syncthreads();
+  const size_t plane = (size_t)E * H;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int ee = i >> 6, hh = i & 63;
+    if (h0 + hh < H && e0 + ee < E) {
+      const float v = tile[hh][ee];
+      const uint16_t hi = f32_to_bf16_rne(v);
+      const float r1 = v - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16_rne(r1);
+      const float r2 = r1 - bf16_to_f32(mid);
+      const uint16_t lo = f32_to_bf16_rne(r2);
+      const size_t o = (size_t)(e0 + ee) * H + h0 + hh;
+      wsplit[o] = hi;
+      wsplit[plane + o] = mid;
+      wsplit[2 * plane + o] = lo;
+    }
+  }
+}
+
+// Block: 4 wavefronts, 128 tokens; wavefront w takes experts 64 w .. 64 w + 63 (two 32-expert
+// tiles) for all 128 tokens (four 32-token tiles), over hidden positions [ks kc, ks kc + kc).
+// MFMA operands straight from memory: lane l holds token (or expert) l % 32 and 8 consecutive
+// hidden positions 8 (l / 32) .. of the 16-position step.  Rows past T or E are clamped (their
+// results are not stored).  No LDS and no barriers: a wavefront with no experts returns.
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wsplit,
+                                                          int T, int H, int E, int kc,
+                                                          float* __restrict__ partial) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e_base = w * 64;
+  if (e_base >= E) return;
+  const int t0 = blockIdx.x * 128, ks = blockIdx.y;
+  const int k_begin = ks * kc, k_end = min(H, k_begin + kc);
+  const int nsteps = (k_end - k_begin) / 16;  // even: kc and H are multiples of 128
+  const int r32 = lane & 31, kg = lane >> 5;
+  const uint16_t* xr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    xr[i] = x + (size_t)min(t0 + i * 32 + r32, T - 1) * H + k_begin + kg * 8;
+  const size_t plane = (size_t)E * H;
+  uint32_t woff[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+    woff[n] = (uint32_t)min(e_base + n * 32 + r32, E - 1) * (uint32_t)H + k_begin + kg * 8;
+  const uint16_t* w0 = wsplit;
+  const uint16_t* w1 = wsplit + plane;
+  const uint16_t* w2 = wsplit + 2 * plane;
+
+  struct Regs {
+    u32x4 a[4];
+    u32x4 b[3][2];
+  };
+  auto load = [&](Regs& r, int step) __attribute__((always_inline)) {
+    const uint32_t k = (uint32_t)step * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(xr[i] + k);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      r.b[0][n] = *reinterpret_cast<const u32x4*>(w0 + (woff[n] + k));
+      r.b[1][n] = *reinterpret_cast<const u32x4*>(w1 + (woff[n] + k));
+      r.b[2][n] = *reinterpret_cast<const u32x4*>(w2 + (woff[n] + k));
+    }
+  };
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][n][v] = 0.f;
+  auto compute = [&](const Regs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 2; p >= 0; --p)  // small pieces first
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, r.a[i]), __builtin_bit_cast(bf16x8, r.b[p][n]),
+              acc[i][n], 0, 0, 0);
+  };
+  // one step of loads in flight behind the MFMAs; the scheduling barriers keep the compiler
+  // from sinking the loads next to their first use
+  Regs r0, r1;
+  load(r0, 0);
+  for (int st = 0; st < nsteps; st += 2) {
+    load(r1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(r0, min(st + 2, nsteps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // accumulator element v of a 32x32 tile: token (v/4)*8 + (lane/32)*4 + v%4, expert lane % 32
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int e = e_base + n * 32 + r32;
+    if (e >= E) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + i * 32 + (v >> 2) * 8 + kg * 4 + (v & 3);
+        if (t < T) partial[((size_t)ks * T + t) * E + e] = acc[i][n][v];
+      }
+  }
+}
+
 // Order-preserving map of a float to an unsigned integer.
 __device__ inline uint32_t ordered_bits(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -204,9 +361,13 @@ __global__ __launch_bounds__(256 * P) void router_select_kernel(
 
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                         int E, int k, float* logits, int32_t* topk_id, float* topk_w,
-                        float* partial, hipStream_t s) {
+                        float* partial, uint16_t* wsplit, hipStream_t s) {
   const RoutePlan p = route_plan(T, H, E);
   dim3 grid(p.tiles, p.KS);
+  if (p.mfma) {
+    router_split_kernel<<<dim3(H / 64, (E + 63) / 64), 256, 0, s>>>(wr, H, E, wsplit);
+    router_mfma_kernel<<<grid, 256, 0, s>>>(x, wsplit, T, H, E, p.kc, partial);
+  } else {
 #define MOE_SLICES(TT_, RG_)                                                                  \
   do {                                                                                        \
     if ((E & 3) == 0)                                                                         \
@@ -223,6 +384,7 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
     default: MOE_SLICES(16, 4); break;
   }
 #undef MOE_SLICES
+  }
   if (p.KS >= 8)
     router_select_kernel<4><<<T, 1024, 0, s>>>(partial, p.KS, bias, T, E, k, logits, topk_id,
                                                topk_w);

@@ -164,6 +164,55 @@ def test_route_stage_zero_input_and_ties():
     assert torch.all(w.cpu() == 1.0 / k)
 
 
+@pytest.mark.parametrize("T,H,E,k,zipf", [
+    (512, 256, 8, 2, None),        # smallest token count of the matrix-core router
+    (513, 384, 40, 4, None),       # ragged token tile, experts not a multiple of 32 or 64
+    (1000, 1024, 256, 8, 1.1),     # Zipf bias, several hidden-dimension slices
+    (700, 7168, 256, 8, None),     # full hidden size
+])
+def test_route_stage_matrix_core(T, H, E, k, zipf):
+    """Router on the matrix cores (many tokens): logits within the fp32 reordering tolerance of
+    the oracle's, top-k ids exact except near-ties, weights to fp32 accuracy."""
+    import bit_expert_ffn_amd as moe
+    print("case route T=%d H=%d E=%d k=%d zipf=%s" % (T, H, E, k, zipf), flush=True)
+    x = synth.make_x(T, H, seed=7)
+    wr = synth.make_router(H, E, seed=7)
+    bias = synth.make_zipf_bias(E, zipf, seed=7) if zipf else None
+    ref_logits = oracle.router(x.view(torch.int16).numpy().view(np.uint16), wr.numpy(),
+                               None if bias is None else bias.numpy())
+    ref_ids, ref_w = oracle.topk(ref_logits, k)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.workspace_size(T, H, 128, E, k), dtype=torch.uint8, device="cuda")
+    moe.route(x.cuda(), wr.cuda(), None if bias is None else bias.cuda(), k, ids, w, ws,
+              logits=logits)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(logits.cpu().numpy() - ref_logits)) <= LOGIT_TOL
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref_logits, ref_w, k)
+
+
+@pytest.mark.parametrize("T,H,E", [(8, 384, 40), (600, 1024, 72)])
+def test_route_one_hot_rows_exact(T, H, E):
+    """x[t] = one-hot at h_t: the logits are row h_t of the router weights, bit for bit (on the
+    matrix-core router this needs the three bf16 pieces of every weight to add up exactly)."""
+    import bit_expert_ffn_amd as moe
+    print("case one-hot route T=%d H=%d E=%d" % (T, H, E), flush=True)
+    g = torch.Generator().manual_seed(T + H + E)
+    h_t = torch.randint(0, H, (T,), generator=g)
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    x[torch.arange(T), h_t] = 1.0
+    wr = torch.randn((H, E), generator=g) * 0.02
+    k = 2
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.workspace_size(T, H, 128, E, k), dtype=torch.uint8, device="cuda")
+    moe.route(x.cuda(), wr.cuda(), None, k, ids, w, ws, logits=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(logits.cpu(), wr[h_t])
+
+
 @pytest.mark.parametrize("E,N,K", [(2, 16, 128), (3, 48, 384), (1, 256, 256)])
 def test_pack_tile_major_bit_exact(E, N, K):
     import bit_expert_ffn_amd as moe
