@@ -53,12 +53,16 @@ def lib():
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
         L.moe_nvfp4_pack.restype = i32
         L.moe_nvfp4_pack.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+        L.moe_layer_nvfp4.restype = i32
+        L.moe_layer_nvfp4.argtypes = [vp, vp, vp, ctypes.POINTER(_Experts), i32, i32, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
-            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_nvfp4_pack")
+            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_nvfp4_pack",
+            "moe_layer_nvfp4")
 
 
 def abi_version():
@@ -222,7 +226,8 @@ class LayerBuffers:
         n = workspace_size(T, H, I, E, k)
         if n == 0:
             raise ValueError("unsupported layer shape T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
-        self.ws = torch.empty(n, dtype=torch.uint8, device=d)
+        # zero-filled: the single-launch layer's counters and flags live in the first 64 KiB
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=d)
 
 
 def layer(x, w_router, bias, experts, k, buf, stream=None):
@@ -234,3 +239,49 @@ def layer(x, w_router, bias, experts, k, buf, stream=None):
                      buf.n_active, k, buf.y, buf.ws, stream=stream)
     combine(buf.y, buf.slot_row, buf.topk_w, buf.out, stream=stream)
     return buf.out
+
+
+def layer_nvfp4(x, w_router, bias, experts, k, buf, stream=None):
+    """moe_layer_nvfp4: the whole layer in one call (one persistent kernel for one or two
+    tokens).  Results are left in `buf` like layer(); buf.y is written only by the four-call
+    path."""
+    prepare_layer_nvfp4(x, w_router, bias, experts, k, buf, stream)()
+    return buf.out
+
+
+def prepare_layer_nvfp4(x, w_router, bias, experts, k, buf, stream=None):
+    """Checks and marshals the arguments of moe_layer_nvfp4 once and returns a callable that
+    makes the call (raising on a non-zero status).  For repeated calls on the same tensors,
+    e.g. a decode loop, where per-call argument checking would cost more host time than the
+    layer takes on the GPU."""
+    T, H = x.shape
+    s = experts_struct(experts)
+    E = s.E
+    if s.H != H or w_router.shape != (H, E):
+        raise ValueError("x, w_router and experts disagree on H or E")
+    y = buf.y
+    yd = MOE_F16 if y.dtype == torch.float16 else MOE_F32
+    n = T * k
+    args = (_dev(x, "x", torch.bfloat16), _dev(w_router, "w_router", torch.float32, (H, E)),
+            None if bias is None else _dev(bias, "bias", torch.float32, (E,)), ctypes.byref(s),
+            T, k, None if buf.logits is None else _dev(buf.logits, "logits", torch.float32, (T, E)),
+            _dev(buf.topk_id, "topk_id", torch.int32, (T, k)),
+            _dev(buf.topk_w, "topk_w", torch.float32, (T, k)),
+            _dev(buf.count, "count", torch.int32, (E,)),
+            _dev(buf.offset, "offset", torch.int32, (E + 1,)),
+            _dev(buf.sorted_slot, "sorted_slot", torch.int32, (n,)),
+            _dev(buf.slot_row, "slot_row", torch.int32, (n,)),
+            _dev(buf.active, "active", torch.int32, (E,)),
+            _dev(buf.n_active, "n_active", torch.int32, (1,)),
+            _dev(y, "y", y.dtype, (n, H)), yd, _dev(buf.out, "out", torch.float32, (T, H)),
+            _dev(buf.ws, "ws", torch.uint8), buf.ws.numel(), _stream(stream, x.device))
+    fn = lib().moe_layer_nvfp4
+    keep = (s,)  # the experts struct must outlive the callable
+
+    def call():
+        code = fn(*args)
+        if code != 0:
+            _check(code, "moe_layer_nvfp4")
+        return keep
+
+    return call

@@ -11,25 +11,31 @@ namespace moe {
 
 WsLayout ws_layout(int T, int H, int I, int E, int k) {
   WsLayout L;
+  // bytes [0, kSyncBytes): the single-launch layer's counters; no other call touches them
+  const size_t base = kSyncBytes;
   const RoutePlan p = route_plan(T, H, E);
-  L.route_partial = 0;
-  L.route_wsplit = align_up((size_t)p.KS * T * E * sizeof(float), 256);
+  L.route_partial = base;
+  L.route_wsplit = base + align_up((size_t)p.KS * T * E * sizeof(float), 256);
   L.route_end = L.route_wsplit;
   if (p.mfma) L.route_end += align_up((size_t)3 * E * H * sizeof(uint16_t), 256);
   const size_t n = (size_t)T * k;
-  L.group_whist = 0;
+  L.group_whist = base;
   L.group_end = 0;
   if (n > (size_t)kGroupSmallMax) {
     const size_t nblk = (n + kGroupChunk - 1) / kGroupChunk;
-    L.group_end = align_up(nblk * 16 * E * sizeof(int32_t), 256);
+    L.group_end = base + align_up(nblk * 16 * E * sizeof(int32_t), 256);
   }
-  L.ffn_x16 = 0;
-  L.ffn_h16 = align_up((size_t)T * H * sizeof(_Float16), 256);
+  L.ffn_x16 = base;
+  L.ffn_h16 = base + align_up((size_t)T * H * sizeof(_Float16), 256);
   L.ffn_tiles = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
   L.ffn_end = L.ffn_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
+  L.ls_partial = base;
+  L.ls_h = base + align_up((size_t)32 * T * E * sizeof(float), 256);
+  L.ls_end = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
   size_t tot = L.route_end;
   if (L.group_end > tot) tot = L.group_end;
   if (L.ffn_end > tot) tot = L.ffn_end;
+  if (L.ls_end > tot) tot = L.ls_end;
   L.total = tot;
   return L;
 }
@@ -168,6 +174,68 @@ MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t
   if (st != MOE_OK) return st;
   return from_hip(moe::launch_combine(y_dev, y_dtype == MOE_F16, slot_row_dev, topk_w_dev, T, k,
                                       H, out_dev, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
+                                   const float* bias_dev, const moe_nvfp4_experts* w, int32_t T,
+                                   int32_t k, float* logits_dev, int32_t* topk_id_dev,
+                                   float* topk_w_dev, int32_t* count_dev, int32_t* offset_dev,
+                                   int32_t* sorted_slot_dev, int32_t* slot_row_dev,
+                                   int32_t* active_dev, int32_t* n_active_dev, void* y_dev,
+                                   int32_t y_dtype, float* out_dev, void* ws_dev,
+                                   size_t ws_bytes, void* stream) {
+  if (!x_dev || !w_router_dev || !w || !topk_id_dev || !topk_w_dev || !count_dev ||
+      !offset_dev || !sorted_slot_dev || !slot_row_dev || !active_dev || !n_active_dev ||
+      !y_dev || !out_dev || !ws_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->gate_q || !w->up_q || !w->down_q || !w->gate_s || !w->up_s || !w->down_s ||
+      !w->tensor_scale)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_F16) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x_dev, w_router_dev, topk_id_dev, topk_w_dev, count_dev, offset_dev,
+                        sorted_slot_dev, slot_row_dev, active_dev, n_active_dev, y_dev, out_dev,
+                        ws_dev, w->gate_q, w->up_q, w->down_q, w->gate_s, w->up_s, w->down_s,
+                        w->tensor_scale};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((bias_dev && !aligned16(bias_dev)) || (logits_dev && !aligned16(logits_dev)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st != MOE_OK) return st;
+  const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int H = w->H, I = w->I, E = w->E;
+  if (moe::layer_small_fits(T, H, I, E, k)) {
+    moe::LayerSmallArgs a;
+    a.x = (const uint16_t*)x_dev;
+    a.wr = w_router_dev;
+    a.bias = bias_dev;
+    a.gq = w->gate_q; a.uq = w->up_q; a.dq = w->down_q;
+    a.gs = w->gate_s; a.us = w->up_s; a.ds = w->down_s;
+    a.ts = w->tensor_scale;
+    a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
+    a.logits = logits_dev;
+    a.topk_id = topk_id_dev; a.topk_w = topk_w_dev;
+    a.count = count_dev; a.offset = offset_dev; a.sorted_slot = sorted_slot_dev;
+    a.slot_row = slot_row_dev; a.active = active_dev; a.n_active = n_active_dev;
+    a.out = out_dev;
+    a.sync = reinterpret_cast<uint32_t*>(ws_dev);
+    a.partial = reinterpret_cast<float*>((char*)ws_dev + L.ls_partial);
+    a.h = reinterpret_cast<uint32_t*>((char*)ws_dev + L.ls_h);
+    const hipError_t e = moe::launch_layer_small(a, (hipStream_t)stream);
+    if (e != hipErrorInvalidConfiguration) return from_hip(e);
+    // the device cannot keep one block per CU resident: run the four calls instead
+  }
+  st = moe_route(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_id_dev, topk_w_dev,
+                 ws_dev, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  st = moe_group(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
+                 active_dev, n_active_dev, ws_dev, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  st = moe_expert_ffn_nvfp4(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
+                            n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_combine(y_dev, y_dtype, slot_row_dev, topk_w_dev, T, k, H, out_dev, stream);
 }
 
 MOE_API moe_status moe_nvfp4_pack(const uint8_t* q_rowmajor_dev, const uint8_t* s_rowmajor_dev,

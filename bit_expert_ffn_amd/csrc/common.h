@@ -32,7 +32,9 @@ constexpr int kRouteMfmaMinT = 512;
 
 RoutePlan route_plan(int T, int H, int E);
 
-// Byte offsets of every call's scratch inside the caller's workspace.
+// Byte offsets of every call's scratch inside the caller's workspace.  The first kSyncBytes
+// hold the single-launch layer's counters and are used by nothing else.
+constexpr size_t kSyncBytes = 65536;
 struct WsLayout {
   size_t route_partial;  // [KS][T][E] fp32
   size_t route_wsplit;   // [3][E][H] bf16 (matrix-core router only)
@@ -43,6 +45,9 @@ struct WsLayout {
   size_t ffn_h16;        // [T*k][I] f16
   size_t ffn_tiles;      // busy-expert tile list: [gemm_max_tiles] int2, then the count (int32)
   size_t ffn_end;
+  size_t ls_partial;     // single-launch layer: [32][T][E] fp32 router partials
+  size_t ls_h;           // single-launch layer: [T*k][I] f16
+  size_t ls_end;
   size_t total;
 };
 WsLayout ws_layout(int T, int H, int I, int E, int k);
@@ -70,6 +75,27 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
                            hipStream_t s);
 int gemm_rows_per_tile(int T);
 size_t gemm_max_tiles(int T, int k, int E);
+
+// Single-launch layer for one or two tokens (layer_small.hip).
+constexpr int kLsMaxSlots = 32;  // most (token, slot) rows of the single-launch layer
+struct LayerSmallArgs {
+  const uint16_t* x;  // [T][H] bf16
+  const float* wr;    // [H][E]
+  const float* bias;  // [E] or null
+  const uint8_t *gq, *uq, *dq, *gs, *us, *ds;  // tile-major NVFP4
+  const float* ts;                             // [E][3]
+  int T, H, I, E, k;
+  float* logits;  // [T][E] or null
+  int32_t *topk_id, *count, *offset, *sorted_slot, *slot_row, *active, *n_active;
+  float* topk_w;
+  float* out;        // [T][H]
+  uint32_t* sync;    // kSyncBytes: counters, flags and an error word, zero between calls
+  float* partial;    // [32][T][E]
+  uint32_t* h;       // [T*k][I/2] f16 pairs
+};
+size_t layer_small_lds(int T, int H, int I, int k);
+bool layer_small_fits(int T, int H, int I, int E, int k);
+hipError_t launch_layer_small(const LayerSmallArgs& a, hipStream_t s);
 
 hipError_t launch_pack(const uint8_t* q_in, const uint8_t* s_in, int E, int N, int K,
                        uint8_t* q_out, uint8_t* s_out, hipStream_t s);

@@ -19,14 +19,9 @@
 // multiplies the final sum once.
 // Activations: x is dotted as bf16 (exact); h is stored as f16 (the down projection's input).
 #include "common.h"
+#include "dot.h"
 
 namespace moe {
-
-constexpr int kChunk = 128;  // K values per chunk (one tile-major column block)
-
-__device__ inline uint32_t load_u16(const uint8_t* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
-}
 
 // ---------------------------------------------------------------------------------------
 // Few-row experts (at most R rows): VALU dot products.  A step's experts are sorted by row
@@ -40,55 +35,6 @@ __device__ inline uint32_t load_u16(const uint8_t* p) {
 // values of each row (two 16-value blocks, each block's sum times its e4m3 scale); the four
 // K-groups of a feature are added by two cross-lane shuffles in a fixed order.
 constexpr int kSet = 4;  // chunks per load set; two sets alternate
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-// 8 values of one code dword dotted with 8 activations (4 pairs), accumulated into acc
-__device__ inline float dot8_bf16(uint32_t q, uint4 xx, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0),
-                                        __builtin_bit_cast(bf16x2_t, xx.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1),
-                                        __builtin_bit_cast(bf16x2_t, xx.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2),
-                                        __builtin_bit_cast(bf16x2_t, xx.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3),
-                                        __builtin_bit_cast(bf16x2_t, xx.w), acc, false);
-  return acc;
-}
-
-__device__ inline float dot8_f16(uint32_t q, uint4 xx, float acc) {
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0),
-                               __builtin_bit_cast(f16x2, xx.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1),
-                               __builtin_bit_cast(f16x2, xx.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2),
-                               __builtin_bit_cast(f16x2, xx.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3),
-                               __builtin_bit_cast(f16x2, xx.w), acc, false);
-  return acc;
-}
-
-// A lane's 32 values (two 16-value scale blocks): each block's dot times its e4m3 scale.
-__device__ inline float dot32_bf16(uint4 q, uint32_t sbytes, const uint4* xv) {
-  const float b0 = dot8_bf16(q.y, xv[1], dot8_bf16(q.x, xv[0], 0.f));
-  const float b1 = dot8_bf16(q.w, xv[3], dot8_bf16(q.z, xv[2], 0.f));
-  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
-         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
-}
-
-__device__ inline float dot32_f16(uint4 q, uint32_t sbytes, const uint4* xv) {
-  const float b0 = dot8_f16(q.y, xv[1], dot8_f16(q.x, xv[0], 0.f));
-  const float b1 = dot8_f16(q.w, xv[3], dot8_f16(q.z, xv[2], 0.f));
-  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
-         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
-}
-
-// the four K-groups of feature n (lanes n, n+16, n+32, n+48), fixed order
-__device__ inline float sum_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
 
 template <int R, int KS>
 __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(

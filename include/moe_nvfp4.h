@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 1
+#define MOE_NVFP4_ABI_VERSION 2
 
 typedef int32_t moe_status;
 enum {
@@ -100,9 +100,14 @@ int32_t moe_abi_version(void);
 const char *moe_status_string(moe_status status);
 
 /* Bytes of device workspace that every call of a layer with these sizes needs (one buffer
- * serves all four calls, which must then be ordered on one stream).  Returns 0 if the sizes are
- * outside the shape limits.  The contents are scratch: no initialisation is needed and calls
- * keep nothing in it from one call to the next. */
+ * serves all calls, which must then be ordered on one stream).  Returns 0 if the sizes are
+ * outside the shape limits.  Apart from its first 64 KiB the contents are scratch: calls keep
+ * nothing there from one call to the next.  The first 64 KiB hold the counters and flags of
+ * moe_layer_nvfp4's single-launch path: they must be zero before the first moe_layer_nvfp4 call
+ * on the buffer (for example, allocate it zero-filled), every completed call leaves them zero,
+ * and no other call reads or writes them.  Word 48 (bytes 192..195) becomes non-zero only if a
+ * wait inside the single-launch kernel timed out; the call's outputs are then undefined and
+ * the 64 KiB must be zeroed again. */
 size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /* Router and top-k ("The model": every token is routed to k of E experts).
@@ -164,6 +169,28 @@ moe_status moe_nvfp4_pack(const uint8_t *q_rowmajor_dev, const uint8_t *s_rowmaj
 moe_status moe_combine(const void *y_dev, int32_t y_dtype, const int32_t *slot_row_dev,
                        const float *topk_w_dev, int32_t T, int32_t k, int32_t H, float *out_dev,
                        void *stream);
+
+/* The whole layer in one call: route, group, expert FFN and combine, with the same arguments,
+ * outputs and meaning as the four calls above (one token: out[t] = sum over the token's k
+ * experts of topk_w * FFN_e(x[t])).
+ * One or two tokens (T*k <= 32 and small enough LDS staging) run as ONE persistent kernel:
+ * every token's expert weights are requested as soon as its routing is known and no launch
+ * gap separates the steps ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU",
+ * section 1 "A megakernel", section 2 "Pipelining everything inside the megakernel").  The
+ * kernel keeps one block per CU resident and its blocks wait for each other through the
+ * counters at the start of ws_dev (see moe_workspace_size).  That path writes logits (if not
+ * NULL), topk_id, topk_w, the grouping arrays and out, but not y; the combine there adds each
+ * token's experts in the order of the active list rather than by slot.
+ * Larger T, or a device that cannot keep one block per CU resident, run the four calls in
+ * order, y_dev ([T*k][H] of y_dtype, grouped row order) holding the expert outputs.
+ * Calls that share ws_dev must not overlap in time. */
+moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const float *bias_dev,
+                           const moe_nvfp4_experts *w, int32_t T, int32_t k, float *logits_dev,
+                           int32_t *topk_id_dev, float *topk_w_dev, int32_t *count_dev,
+                           int32_t *offset_dev, int32_t *sorted_slot_dev, int32_t *slot_row_dev,
+                           int32_t *active_dev, int32_t *n_active_dev, void *y_dev,
+                           int32_t y_dtype, float *out_dev, void *ws_dev, size_t ws_bytes,
+                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     for code in (OK, INVALID, SHAPE, WS, -4, -5, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
 
@@ -144,3 +144,31 @@ def test_pack_rejects_bad_arguments():
     assert p(A, B, 2, 24, 128, C, D, None) == SHAPE
     assert p(A, B, 2, 16, 96, C, D, None) == SHAPE
     assert p(A, B, 2, 16, 128, A, D, None) == INVALID  # in place
+
+
+def _layer(**over):
+    ex = moe._Experts(A, A, A, A, A, A, A, 8, 256, 128)
+    a = dict(x=A, wr=A, bias=None, ex=ex, T=1, k=2, logits=None, out=A, y=A, ydt=0, ws=A,
+             ws_bytes=1 << 30, topk=A)
+    a.update(over)
+    return moe.lib().moe_layer_nvfp4(a["x"], a["wr"], a["bias"], ctypes.byref(a["ex"]), a["T"],
+                                     a["k"], a["logits"], a["topk"], A, A, A, A, A, A, A, a["y"],
+                                     a["ydt"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_layer_rejects_bad_arguments():
+    assert _layer(x=None) == INVALID
+    assert _layer(out=None) == INVALID
+    assert _layer(y=None) == INVALID
+    assert _layer(topk=A + 4) == INVALID
+    assert _layer(ydt=5) == INVALID
+    assert _layer(k=9) == INVALID
+    assert _layer(ex=moe._Experts(A, A, A, A, A, A, None, 8, 256, 128)) == INVALID
+    assert _layer(ex=moe._Experts(A, A, A, A, A, A, A, 8, 250, 128)) == SHAPE
+    assert _layer(ws_bytes=1024) == WS
+
+
+def test_workspace_leaves_room_for_the_sync_words():
+    # the single-launch layer's counters and flags occupy the first 64 KiB; every region follows
+    for T in (1, 2, 64):
+        assert moe.workspace_size(T, 7168, 2048, 256, 8) >= 65536 + T * 7168 * 2

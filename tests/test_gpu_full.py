@@ -94,6 +94,24 @@ def test_decode1_full():
         _check_tokens(sp, L, ex_host, buf, [0], L["x"], t_offset=t)
 
 
+def test_decode1_full_single_launch():
+    """The benchmark's decode configuration: one call of moe_layer_nvfp4 per token (a single
+    persistent kernel), pool tokens 0..3 on one workspace."""
+    import bit_expert_ffn_amd as moe
+    sp, L, ex_host = _layer("decode1")
+    print("case decode1 single launch T=1 H=7168 I=2048 E=256 k=8", flush=True)
+    ex = L.setdefault("_packed", None) or moe.pack_experts(L["experts"])
+    L["_packed"] = ex
+    buf = moe.LayerBuffers(1, sp["H"], sp["I"], sp["E"], sp["k"], device="cuda",
+                           y_dtype=torch.float16)
+    for t in range(4):
+        moe.layer_nvfp4(L["x"][t:t + 1], L["w_router"], L["bias"], ex, sp["k"], buf)
+        torch.cuda.synchronize()
+        assert not buf.ws[:65536].any().item(), "counters or flags not reset"
+        _check_group_invariants(buf, sp["E"], sp["k"])
+        _check_tokens(sp, L, ex_host, buf, [0], L["x"], t_offset=t)
+
+
 def test_decode64_full():
     sp, L, ex_host = _layer("decode64")
     print("case decode64 T=64", flush=True)
