@@ -1,10 +1,13 @@
 """Benchmark of one NVFP4 sparse-MoE FFN layer on one MI355X.
 
-A step is one pass of the whole layer (moe_route -> moe_group -> moe_expert_ffn_nvfp4 ->
-moe_combine) over one batch of seeded synthetic tokens whose inputs are already resident in
-HBM.  Prints one JSON line (the benchmark contract) with the layer throughput, the roofline of
-the expert-FFN call (the kernel work that streams the expert weights) measured with HIP events
-on the launch stream over the timed region, and the CPU oracle timed on a bounded sample.
+A step is one pass of the whole layer over one batch of seeded synthetic tokens whose inputs
+are already resident in HBM: for one or two tokens one moe_layer_nvfp4 call (a single
+persistent kernel), otherwise moe_route -> moe_group -> moe_expert_ffn_nvfp4 -> moe_combine.
+Prints one JSON line (the benchmark contract) with the layer throughput; the roofline of the
+dominant kernel work, timed with HIP events on the launch stream over the timed region (the
+single-launch kernel, or the expert-FFN call of the four-call path); its HBM traffic from the
+committed PMC summary when the kernel is unchanged since; and the CPU oracle timed on a
+bounded sample.
 
 Workloads (hidden 7168, 256 experts, top-8, NVFP4 experts):
   decode1     T=1, expert intermediate 2048; each step takes the next token of a seeded pool of
@@ -143,20 +146,23 @@ def main():
     ffn_bytes = w_bytes + T * H * 2 + T * k * H * 2          # weights + x + y (f16)
     layer_bytes = w_bytes + T * H * 2 + H * E * 4 + T * H * 4  # weights + x + router + out
     flops = 6.0 * T * k * H * I
+    traffic = None
     if fused:
         # the single kernel reads the expert weights, x and the router weights, writes out
         kernel, kbytes = "layer_small_kernel", layer_bytes
+        if wl == "decode1":
+            traffic = measured_traffic("traffic_layer_small_decode1.txt")
     else:
         kernel, kbytes = "expert FFN call (few-row kernels + grouped GEMM)", ffn_bytes
     if big:
         achieved = flops / (ffn_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_F16_PEAK_TFS,
-                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFS, 4), traffic=None,
+                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFS, 4), traffic=traffic,
                     kernel=kernel)
     else:
         achieved = kbytes / (ffn_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel=kernel)
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -180,6 +186,29 @@ def main():
         "ffn_flops": flops,
     }
     print(json.dumps(res))
+
+
+def measured_traffic(kernel_file):
+    """HBM bytes per launch from the committed PMC summary of this kernel, if the kernel's
+    sources are unchanged since the counters were taken (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["sources"].split():
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != fields["sha256"]:
+            return None
+        return int(fields["bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def cpu_baseline(layer, sp, pool, budget_s):
