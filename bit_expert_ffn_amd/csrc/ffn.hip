@@ -28,9 +28,10 @@ namespace moe {
 // count and the few-row ones run in their own loop, apart from the busy experts' path
 // ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", section 5 "Keeping register
 // pressure off the common path"); most experts of a decode step serve one or two rows.
-// Block: 4 wavefronts, one 16-feature tile each, over the whole K.  The expert's activation
-// rows are staged once in LDS; each lane keeps up to 2 * kSet chunks of packed weights in
-// flight: two register sets alternate, one loading while the other is used.  Lane l = 16*g + n
+// Block: 4 wavefronts, one 16-feature tile each, over the whole K.  The first weights are
+// requested as soon as the expert is known; the expert's activation rows are then staged once
+// in LDS; each lane keeps up to 2 * kSet chunks of packed weights in flight: two register sets
+// alternate, one loading while the other is used.  Lane l = 16*g + n
 // decodes its 32 values of feature n per chunk and dots them with the matching 32 activation
 // values of each row (two 16-value blocks, each block's sum times its e4m3 scale); the four
 // K-groups of a feature are added by two cross-lane shuffles in a fixed order.
@@ -49,20 +50,9 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
   const int slot = blockIdx.y;
   if (slot >= *n_active) return;
   const int e = active[slot];
-  const int rows = count[e];
-  if (rows > R) return;  // a busy expert: the matrix-core path takes it
-  const int base = offset[e];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int ks = wv % KS;  // this wavefront's K slice of its tile
-  // stage the expert's activation rows
-  for (int r = 0; r < rows; ++r) {
-    const int tok = sorted_slot[base + r] / k;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok * H);
-    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)r * H);
-    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
-  }
-  __syncthreads();
   const int rt = blockIdx.x * (4 / KS) + wv / KS;  // 16-feature row tile
   const int nchunk_all = H / kChunk;
   // balanced split: the host keeps KS <= nchunk_all, so every slice has at least one chunk
@@ -86,6 +76,20 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       su[u] = load_u16(usp + c * 128);
     }
   };
+  // the first weights depend only on the expert: request them before the chain of dependent
+  // loads (row count, offsets, token ids, activations) that staging the rows needs
+  load_set(qgA, quA, sgA, suA, 0);
+  const int rows = count[e];
+  if (rows > R) return;  // a busy expert: the matrix-core path takes it
+  const int base = offset[e];
+  // stage the expert's activation rows
+  for (int r = 0; r < rows; ++r) {
+    const int tok = sorted_slot[base + r] / k;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok * H);
+    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)r * H);
+    for (int i = threadIdx.x; i < H / 8; i += 256) dst[i] = src[i];
+  }
+  lds_barrier();
   float ag[R], au[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) ag[r] = au[r] = 0.f;
@@ -106,7 +110,6 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       }
     }
   };
-  load_set(qgA, quA, sgA, suA, 0);
   for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
     load_set(qgB, quB, sgB, suB, c0 + kSet);
     use_set(qgA, quA, sgA, suA, c0);
@@ -165,18 +168,9 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
   const int slot = blockIdx.y;
   if (slot >= *n_active) return;
   const int e = active[slot];
-  const int rows = count[e];
-  if (rows > R) return;
-  const int base = offset[e];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int ks = wv % KS;
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(h16 + (size_t)base * I);
-    uint4* dst = reinterpret_cast<uint4*>(hs);
-    for (int i = threadIdx.x; i < rows * I / 8; i += 256) dst[i] = src[i];
-  }
-  __syncthreads();
   const int rt = blockIdx.x * (4 / KS) + wv / KS;
   const int nchunk_all = I / kChunk;
   const int cbeg = ks * nchunk_all / KS;
@@ -194,6 +188,17 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
       sc[u] = load_u16(sp + c * 128);
     }
   };
+  // first weights before the dependent loads that staging h needs
+  load_set(qA, sA, 0);
+  const int rows = count[e];
+  if (rows > R) return;
+  const int base = offset[e];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(h16 + (size_t)base * I);
+    uint4* dst = reinterpret_cast<uint4*>(hs);
+    for (int i = threadIdx.x; i < rows * I / 8; i += 256) dst[i] = src[i];
+  }
+  lds_barrier();
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -209,7 +214,6 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
       }
     }
   };
-  load_set(qA, sA, 0);
   for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
     load_set(qB, sB, c0 + kSet);
     use_set(qA, sA, c0);

@@ -165,14 +165,17 @@ def test_route_stage_zero_input_and_ties():
 
 
 @pytest.mark.parametrize("T,H,E,k,zipf", [
+    (64, 256, 8, 2, None),         # below the matrix-core router: fp32 slices
+    (128, 7168, 256, 8, 1.1),      # the verify shape (fp32 slices)
     (512, 256, 8, 2, None),        # smallest token count of the matrix-core router
     (513, 384, 40, 4, None),       # ragged token tile, experts not a multiple of 32 or 64
     (1000, 1024, 256, 8, 1.1),     # Zipf bias, several hidden-dimension slices
     (700, 7168, 256, 8, None),     # full hidden size
 ])
 def test_route_stage_matrix_core(T, H, E, k, zipf):
-    """Router on the matrix cores (many tokens): logits within the fp32 reordering tolerance of
-    the oracle's, top-k ids exact except near-ties, weights to fp32 accuracy."""
+    """Router around and above the switch to the matrix cores (512 tokens): logits within the
+    fp32 reordering tolerance of the oracle's, top-k ids exact except near-ties, weights to fp32
+    accuracy."""
     import bit_expert_ffn_amd as moe
     print("case route T=%d H=%d E=%d k=%d zipf=%s" % (T, H, E, k, zipf), flush=True)
     x = synth.make_x(T, H, seed=7)
