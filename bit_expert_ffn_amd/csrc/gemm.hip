@@ -85,22 +85,23 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     ffn_plan(count, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
-// Block: 256 threads = 2 x 2 wavefronts; MT = 64 * WM rows x 256 weight rows; K in stages of
-// 64.  Wavefront (wm, wn) computes rows wm * 32 * WM .. (WM tiles of 32) against 4 weight tiles
-// of 32 rows:
-//   gate/up: gate rows f0 + 64 wn + {0, 32} and the same up rows -> 64 features per wavefront,
-//            128 per block, h = silu(g) * u in the epilogue;
-//   down:    rows n0 + 128 wn + {0, 32, 64, 96} -> 256 output features per block.
-// Activations go through LDS (double buffered, rows padded to 144 bytes).  Weights do not: each
-// lane loads, per stage and per weight tile, the 16 packed bytes (32 codes) of weight row
-// l % 32 and K-group 2 (st % 2) + l / 32 of the stage's 128-column chunk, plus two scale bytes,
-// and decodes one code dword right before each of the stage's four 16-K MFMA steps.  The MFMA
-// sums over its 16 k positions, so K may be permuted: step i takes codes 8i..8i+7 of the
-// lane's group, and the activation operand is read from LDS columns 32 (l / 32) + 8i of the
-// stage (same permutation).  Global loads of activations and packed weights run ahead in two
-// register sets (even / odd stages).
-template <bool GATEUP, int WM, bool Y_F16>
-__global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
+// Block: 256 threads = 4 wavefronts side by side in N; MT = 64 * WM rows x 256 weight rows; K
+// in stages of 64.  Every wavefront computes all MT rows (MI = MT / 32 tiles of 32) against its
+// own 2 weight tiles of 32 rows:
+//   gate/up: wavefront wn takes features f0 + 32 wn .. + 31 of the block's 128: its gate tile
+//            and the up tile of the same features; h = silu(g) * u in the epilogue;
+//   down:    rows n0 + 64 wn + {0, 32} -> 256 output features per block.
+// Each weight byte is loaded and decoded by one wavefront only, and each decoded fragment feeds
+// MI MFMAs.  Activations go through LDS (double buffered, rows padded to 144 bytes) and every
+// wavefront reads all of them.  Weights do not: each lane loads, per stage and per weight
+// tile, the 16 packed bytes (32 codes) of weight row l % 32 and K-group 2 (st % 2) + l / 32 of
+// the stage's 128-column chunk, plus its two scale bytes, and decodes one code dword right
+// before each of the stage's four 16-K MFMA steps.  The MFMA sums over its 16 k positions, so
+// K may be permuted: step i takes codes 8i..8i+7 of the lane's group, and the activation
+// operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
+// loads of activations and packed weights run ahead in S register sets.
+template <bool GATEUP, int WM, bool Y_F16, int S>
+__global__ __launch_bounds__(256, S == 2 ? 2 : 1) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
@@ -108,8 +109,8 @@ __global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
     const int32_t* __restrict__ sorted_slot, const int2* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out) {
   constexpr int MT = 64 * WM;
-  constexpr int NA = 2 * WM;  // 16-byte activation pieces per thread per stage
-  constexpr int NT = 4;       // weight tiles of 32 rows per wavefront
+  constexpr int MI = MT / 32;  // 32-row tiles per wavefront
+  constexpr int NA = MT / 32;  // 16-byte activation pieces per thread per stage
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native vector: stays in VGPRs
   __shared__ __attribute__((aligned(16))) _Float16 As[2][MT][gLD];
   // Block order.  Workgroups go round-robin to the 8 XCDs, each with its own L2; renumber so
@@ -144,25 +145,22 @@ __global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
   const int N = GATEUP ? I : H;  // rows of one weight matrix
   const int nchunk = K / 128;
   const int nstage = K / gK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
 
   // activation rows of this thread's pieces (rows past the expert's end repeat its last row:
   // their outputs are never stored).  Offsets are 32-bit element offsets from a uniform base
   // (x and h are far below 2^32 elements), which keeps the per-lane state small.
-  auto aoff_of = [&](int i) __attribute__((always_inline)) {
-    const int s = tid + 256 * i;
-    const int r = min(m0 + (s >> 3), rows - 1);
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int sidx = tid + 256 * i;
+    const int r = min(m0 + (sidx >> 3), rows - 1);
     const uint32_t src = GATEUP ? (uint32_t)(sorted_slot[base + r] / k) * (uint32_t)H
                                 : (uint32_t)(base + r) * (uint32_t)I;
-    return src + (uint32_t)(s & 7) * 8;
-  };
-  const uint32_t aoff0 = aoff_of(0);
-  const uint32_t aoff1 = aoff_of(1);
-  const uint32_t aoff2 = NA > 2 ? aoff_of(2) : aoff0;
-  const uint32_t aoff3 = NA > 2 ? aoff_of(3) : aoff0;
+    aoff[i] = src + (uint32_t)(sidx & 7) * 8;
+  }
 
-  // weight rows of this lane in its 4 weight tiles; rows past N (only possible in the last
+  // weight rows of this lane in its 2 weight tiles; rows past N (only possible in the last
   // block of down when H % 256 != 0) re-read row N - 1 and are never stored.  Byte offsets
   // within the expert's matrix (< 2^32) from uniform bases.
   const int r32 = lane & 31, hgrp = lane >> 5;
@@ -170,108 +168,97 @@ __global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
   const uint8_t* sb0 = sm0 + (size_t)e * ((size_t)N * K / 16);
   const uint8_t* qb1 = GATEUP ? qm1 + (size_t)e * ((size_t)N * K / 2) : qb0;
   const uint8_t* sb1 = GATEUP ? sm1 + (size_t)e * ((size_t)N * K / 16) : sb0;
-  uint32_t qoff[NT], soff[NT];
-  int feat[NT];
+  uint32_t qoff[2], soff[2];
+  int feat[2];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int row = GATEUP ? fb * 128 + wn * 64 + (t & 1) * 32 + r32
-                           : fb * 256 + wn * 128 + t * 32 + r32;
+  for (int t = 0; t < 2; ++t) {
+    const int row = GATEUP ? fb * 128 + wn * 32 + r32 : fb * 256 + wn * 64 + t * 32 + r32;
     feat[t] = row;
     const int rc = min(row, N - 1);
     const uint32_t tile0 = (uint32_t)(rc >> 4) * (uint32_t)nchunk;
     qoff[t] = tile0 * 1024u + (uint32_t)(rc & 15) * 16u + (uint32_t)hgrp * 256u;
     soff[t] = tile0 * 128u + (uint32_t)(rc & 15) * 2u + (uint32_t)hgrp * 32u;
   }
-  auto qbase = [&](int t) __attribute__((always_inline)) { return (GATEUP && t >= 2) ? qb1 : qb0; };
-  auto sbase = [&](int t) __attribute__((always_inline)) { return (GATEUP && t >= 2) ? sb1 : sb0; };
+  const uint8_t* qbt1 = GATEUP ? qb1 : qb0;  // tile 1: the up matrix (gate/up) or down again
+  const uint8_t* sbt1 = GATEUP ? sb1 : sb0;
 
   struct Stage {
-    u32x4 a0, a1, a2, a3;
-    u32x4 q0, q1, q2, q3;
-    uint32_t s0, s1, s2, s3;
+    u32x4 a[NA];
+    u32x4 q0, q1;
+    uint32_t s0, s1;
   };
   auto load = [&](Stage& r, int st) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)st * gK;
-    r.a0 = *reinterpret_cast<const u32x4*>(xa + (aoff0 + k0));
-    r.a1 = *reinterpret_cast<const u32x4*>(xa + (aoff1 + k0));
-    if (NA > 2) {
-      r.a2 = *reinterpret_cast<const u32x4*>(xa + (aoff2 + k0));
-      r.a3 = *reinterpret_cast<const u32x4*>(xa + (aoff3 + k0));
-    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(xa + (aoff[i] + k0));
     // tile-lane of this lane's K-group in the stage's chunk: 16 * g + row % 16, where
     // g = 2 (st % 2) + lane / 32 (the lane / 32 part is already in qoff / soff)
     const uint32_t cq = (uint32_t)(st >> 1) * 1024u + (uint32_t)(st & 1) * 512u;
     const uint32_t cs = (uint32_t)(st >> 1) * 128u + (uint32_t)(st & 1) * 64u;
-    r.q0 = *reinterpret_cast<const u32x4*>(qbase(0) + (qoff[0] + cq));
-    r.q1 = *reinterpret_cast<const u32x4*>(qbase(1) + (qoff[1] + cq));
-    r.q2 = *reinterpret_cast<const u32x4*>(qbase(2) + (qoff[2] + cq));
-    r.q3 = *reinterpret_cast<const u32x4*>(qbase(3) + (qoff[3] + cq));
-    r.s0 = *reinterpret_cast<const uint16_t*>(sbase(0) + (soff[0] + cs));
-    r.s1 = *reinterpret_cast<const uint16_t*>(sbase(1) + (soff[1] + cs));
-    r.s2 = *reinterpret_cast<const uint16_t*>(sbase(2) + (soff[2] + cs));
-    r.s3 = *reinterpret_cast<const uint16_t*>(sbase(3) + (soff[3] + cs));
+    r.q0 = *reinterpret_cast<const u32x4*>(qb0 + (qoff[0] + cq));
+    r.q1 = *reinterpret_cast<const u32x4*>(qbt1 + (qoff[1] + cq));
+    // the lane's two scale bytes sit in the low (even row) or high (odd row) half of an aligned
+    // dword; loading the whole dword keeps the value free of any zero-extension, which the
+    // compiler would otherwise place right after the load (in the previous step) and so wait
+    // for every load in flight
+    r.s0 = *reinterpret_cast<const uint32_t*>(sb0 + ((soff[0] + cs) & ~3u));
+    r.s1 = *reinterpret_cast<const uint32_t*>(sbt1 + ((soff[1] + cs) & ~3u));
   };
   auto store_a = [&](const Stage& r, int buf) __attribute__((always_inline)) {
     // piece i of this thread: s = tid + 256 * i -> row s >> 3, 16-byte column s & 7
     const int c8 = (tid & 7) * 8;
-    *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3)][c8]) = r.a0;
-    *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32][c8]) = r.a1;
-    if (NA > 2) {
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 64][c8]) = r.a2;
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 96][c8]) = r.a3;
-    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32 * i][c8]) = r.a[i];
   };
 
-  f32x16 acc[WM][NT];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][t][v] = 0.f;
-  auto bfrag = [&](u32x4 q, uint32_t sbytes, int step) __attribute__((always_inline)) {
-    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbytes, 1.0f, false);
+  const bool odd_row = (r32 & 1) != 0;  // which half of the scale dword is this lane's
+  auto bfrag = [&](u32x4 q, uint32_t sdword, int step) __attribute__((always_inline)) {
+    const f16x2 sc = odd_row ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sdword, 1.0f, true)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sdword, 1.0f, false);
     const f16x2 sv = step < 2 ? f16x2{sc[0], sc[0]} : f16x2{sc[1], sc[1]};
     return gdecode8(q[step], sv);
   };
   auto compute = [&](const Stage& r, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
-      f16x8 a[WM];
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(
-            &As[buf][wm * 32 * WM + i * 32 + r32][hgrp * 32 + step * 8]);
       const f16x8 b0 = bfrag(r.q0, r.s0, step);
       const f16x8 b1 = bfrag(r.q1, r.s1, step);
-      const f16x8 b2 = bfrag(r.q2, r.s2, step);
-      const f16x8 b3 = bfrag(r.q3, r.s3, step);
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b1, acc[i][1], 0, 0, 0);
-        acc[i][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b2, acc[i][2], 0, 0, 0);
-        acc[i][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b3, acc[i][3], 0, 0, 0);
+      for (int i = 0; i < MI; ++i) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&As[buf][i * 32 + r32][hgrp * 32 + step * 8]);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[i][1], 0, 0, 0);
       }
     }
   };
 
-  // pipeline: nstage = K / 64 is even (K is a multiple of 128), so the loop body has no
-  // conditions; the loads past the last stage re-read it (clamped) and are unused.
-  Stage r0, r1;
-  load(r0, 0);
-  load(r1, 1);
-  store_a(r0, 0);
+  // pipeline over S register sets (nstage is a multiple of S, so the loop body has no
+  // conditions; loads past the last stage re-read it, clamped, and are unused).  Set j holds
+  // stage s = st + j: its weights feed compute, and right after it the set is refilled with
+  // stage s + S; the activations of stage s + 1 (loaded S - 1 steps earlier) go to the other
+  // LDS buffer.  With S = 4 loads run three stages ahead.
+  Stage r[S];
+  const int last = nstage - 1;
+#pragma unroll
+  for (int jj = 0; jj < S; ++jj) load(r[jj], min(jj, last));
+  store_a(r[0], 0);
   lds_barrier();
-  for (int st = 0; st < nstage; st += 2) {
-    compute(r0, 0);
-    store_a(r1, 1);
-    load(r0, min(st + 2, nstage - 1));
-    lds_barrier();
-    compute(r1, 1);
-    store_a(r0, 0);
-    load(r1, min(st + 3, nstage - 1));
-    lds_barrier();
+  for (int st = 0; st < nstage; st += S) {
+#pragma unroll
+    for (int jj = 0; jj < S; ++jj) {
+      compute(r[jj], jj & 1);
+      store_a(r[(jj + 1) % S], (jj + 1) & 1);
+      load(r[jj], min(st + jj + S, last));
+      lds_barrier();
+    }
   }
 
   // epilogue; accumulator element v of a 32x32 tile: row (v/4)*8 + (lane/32)*4 + v%4, col lane%32
@@ -279,31 +266,28 @@ __global__ __launch_bounds__(256, WM == 2 ? 2 : 1) void ffn_gemm_kernel(
   if (GATEUP) {
     const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
     _Float16* h16 = reinterpret_cast<_Float16*>(out);
+    const int f = feat[0];  // the gate tile and the up tile hold the same features
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int f = feat[t];  // gate tile t and up tile t + 2 hold the same features
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 32 * WM + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
-          if (m < rows) {
-            const float gv = acc[i][t][v] * tsg, uv = acc[i][t + 2][v] * tsu;
-            h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
-          }
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
+        if (m < rows) {
+          const float gv = acc[i][0][v] * tsg, uv = acc[i][1][v] * tsu;
+          h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
         }
       }
   } else {
     const float tsd = ts[e * 3 + 2];
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < 2; ++t) {
         const int f = feat[t];
         if (f >= N) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 32 * WM + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
+          const int m = m0 + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
           if (m < rows) {
             const float yv = acc[i][t][v] * tsd;
             const size_t o = (size_t)(base + m) * H + f;
@@ -334,10 +318,19 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
   x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
       a.x, a.x16, n8, a.count, a.active, a.n_active, MT, min_rows, tiles, max_tiles, n_tiles);
   const dim3 gg(a.I / 128, max_tiles), gd((a.H + 255) / 256, max_tiles);
+#define MOE_GEMM_S(GU_, WM_, F16_, S_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                  \
+  ffn_gemm_kernel<GU_, WM_, F16_, S_><<<GRID_, 256, 0, s>>>(XA_, Q0_, S0_, Q1_, S1_, a.ts,      \
+                                                            a.count, a.offset, a.sorted_slot,   \
+                                                            tiles, n_tiles, a.k, a.H, a.I, OUT_)
+  // 64-row tiles (one wavefront per SIMD either way): four register sets when the stage count
+  // allows it; 128-row tiles keep two sets, which leaves room for two wavefronts per SIMD
 #define MOE_GEMM(GU_, WM_, F16_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
-  ffn_gemm_kernel<GU_, WM_, F16_><<<GRID_, 256, 0, s>>>(XA_, Q0_, S0_, Q1_, S1_, a.ts,          \
-                                                        a.count, a.offset, a.sorted_slot,       \
-                                                        tiles, n_tiles, a.k, a.H, a.I, OUT_)
+  do {                                                                                        \
+    if (WM_ == 1 && ((GU_ ? a.H : a.I) / gK) % 4 == 0)                                        \
+      MOE_GEMM_S(GU_, WM_, F16_, 4, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_);                    \
+    else                                                                                      \
+      MOE_GEMM_S(GU_, WM_, F16_, 2, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_);                    \
+  } while (0)
   if (MT == 128) {
     MOE_GEMM(true, 2, false, gg, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
     if (a.y_f16) MOE_GEMM(false, 2, true, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
@@ -348,6 +341,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
     else MOE_GEMM(false, 1, false, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
   }
 #undef MOE_GEMM
+#undef MOE_GEMM_S
   return hipGetLastError();
 }
 
