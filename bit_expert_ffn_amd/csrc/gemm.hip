@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
 // operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
 // loads of activations and packed weights run ahead in S register sets.
 template <bool GATEUP, int WM, bool Y_F16, int S>
-__global__ __launch_bounds__(256, S == 2 ? 2 : 1) void ffn_gemm_kernel(
+__global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
@@ -240,23 +240,33 @@ __global__ __launch_bounds__(256, S == 2 ? 2 : 1) void ffn_gemm_kernel(
     }
   };
 
-  // pipeline over S register sets (nstage is a multiple of S, so the loop body has no
-  // conditions; loads past the last stage re-read it, clamped, and are unused).  Set j holds
-  // stage s = st + j: its weights feed compute, and right after it the set is refilled with
-  // stage s + S; the activations of stage s + 1 (loaded S - 1 steps earlier) go to the other
-  // LDS buffer.  With S = 4 loads run three stages ahead.
+  // pipeline over S register sets.  Set j holds stage s = st + j: its weights feed compute,
+  // and right after it the set is refilled with stage s + S; the activations of stage s + 1
+  // (loaded S - 1 steps earlier) go to the other LDS buffer, so loads run S - 1 stages ahead.
+  // The main loop covers the largest multiple of S stages with no conditions in its body
+  // (loads past the last stage re-read it, clamped, and are unused); the remaining stages
+  // (fewer than S) follow, each guarded by a uniform condition.
   Stage r[S];
   const int last = nstage - 1;
+  const int nmain = nstage - nstage % S;
 #pragma unroll
   for (int jj = 0; jj < S; ++jj) load(r[jj], min(jj, last));
   store_a(r[0], 0);
   lds_barrier();
-  for (int st = 0; st < nstage; st += S) {
+  for (int st = 0; st < nmain; st += S) {
 #pragma unroll
     for (int jj = 0; jj < S; ++jj) {
-      compute(r[jj], jj & 1);
-      store_a(r[(jj + 1) % S], (jj + 1) & 1);
+      compute(r[jj], (st + jj) & 1);
+      store_a(r[(jj + 1) % S], (st + jj + 1) & 1);
       load(r[jj], min(st + jj + S, last));
+      lds_barrier();
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < S - 1; ++jj) {
+    if (nmain + jj < nstage) {
+      compute(r[jj], (nmain + jj) & 1);
+      store_a(r[(jj + 1) % S], (nmain + jj + 1) & 1);
       lds_barrier();
     }
   }
@@ -322,15 +332,10 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
   ffn_gemm_kernel<GU_, WM_, F16_, S_><<<GRID_, 256, 0, s>>>(XA_, Q0_, S0_, Q1_, S1_, a.ts,      \
                                                             a.count, a.offset, a.sorted_slot,   \
                                                             tiles, n_tiles, a.k, a.H, a.I, OUT_)
-  // 64-row tiles (one wavefront per SIMD either way): four register sets when the stage count
-  // allows it; 128-row tiles keep two sets, which leaves room for two wavefronts per SIMD
+  // 64-row tiles: four register sets; 128-row tiles: three, which still leaves room for two
+  // wavefronts per SIMD
 #define MOE_GEMM(GU_, WM_, F16_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
-  do {                                                                                        \
-    if (WM_ == 1 && ((GU_ ? a.H : a.I) / gK) % 4 == 0)                                        \
-      MOE_GEMM_S(GU_, WM_, F16_, 4, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_);                    \
-    else                                                                                      \
-      MOE_GEMM_S(GU_, WM_, F16_, 2, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_);                    \
-  } while (0)
+  MOE_GEMM_S(GU_, WM_, F16_, (WM_ == 1 ? 4 : 3), GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)
   if (MT == 128) {
     MOE_GEMM(true, 2, false, gg, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
     if (a.y_f16) MOE_GEMM(false, 2, true, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
