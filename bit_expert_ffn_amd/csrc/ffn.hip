@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
     const uint8_t* __restrict__ us, const float* __restrict__ ts,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16) {
+    const int32_t* __restrict__ n_active, int k, int H, int I, _Float16* __restrict__ h16,
+    int early) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [R][H] bf16
   __shared__ float red[4][R][2][16];
   const int slot = blockIdx.y;
@@ -76,11 +77,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       su[u] = load_u16(usp + c * 128);
     }
   };
-  // the first weights depend only on the expert: request them before the chain of dependent
-  // loads (row count, offsets, token ids, activations) that staging the rows needs
-  load_set(qgA, quA, sgA, suA, 0);
+  // the first weights depend only on the expert: with few tokens (early != 0) request them
+  // before the chain of dependent loads (row count, offsets, token ids, activations) that
+  // staging the rows needs; with many tokens most experts are busy, so check the count first
+  if (early) load_set(qgA, quA, sgA, suA, 0);
   const int rows = count[e];
   if (rows > R) return;  // a busy expert: the matrix-core path takes it
+  if (!early) load_set(qgA, quA, sgA, suA, 0);
   const int base = offset[e];
   // stage the expert's activation rows
   for (int r = 0; r < rows; ++r) {
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
     const uint8_t* __restrict__ dsc, const float* __restrict__ ts,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int H, int I,
-    void* __restrict__ y) {
+    void* __restrict__ y, int early) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hs[];  // [R][I] f16
   __shared__ float red[4][R][16];
   const int slot = blockIdx.y;
@@ -188,10 +191,11 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
       sc[u] = load_u16(sp + c * 128);
     }
   };
-  // first weights before the dependent loads that staging h needs
-  load_set(qA, sA, 0);
+  // first weights before the dependent loads that staging h needs (few tokens only)
+  if (early) load_set(qA, sA, 0);
   const int rows = count[e];
   if (rows > R) return;
+  if (!early) load_set(qA, sA, 0);
   const int base = offset[e];
   {
     const uint4* src = reinterpret_cast<const uint4*>(h16 + (size_t)base * I);
@@ -273,6 +277,8 @@ hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream
   const int maxe = a.E < a.T * a.k ? a.E : a.T * a.k;
   const int R = few_rows(a.T, a.H, a.I);
   const bool heavy = a.T > R;  // some expert may have more than R rows
+  // with few tokens nearly every expert is few-row: request weights before checking the count
+  const int early = (size_t)a.T * a.k <= (size_t)4 * a.E ? 1 : 0;
   // gate/up + SwiGLU
   if (R > 0) {
     const int ks = few_ksplit(maxe * (a.I / 16), a.H / kChunk);
@@ -282,7 +288,7 @@ hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream
   ffn_gateup_few_kernel<R_, KS_><<<grid, 256, lds, s>>>(a.x, a.gq, a.uq, a.gs, a.us, a.ts,   \
                                                         a.count, a.offset, a.sorted_slot,    \
                                                         a.active, a.n_active, a.k, a.H, a.I, \
-                                                        a.h16)
+                                                        a.h16, early)
 #define MOE_FEW_GU_R(R_)                 \
   do {                                   \
     if (ks == 4) MOE_FEW_GU(R_, 4);      \
@@ -303,7 +309,7 @@ hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream
 #define MOE_FEW_D(R_, KS_, F16_)                                                                 \
   ffn_down_few_kernel<R_, KS_, F16_><<<grid, 256, lds, s>>>(a.h16, a.dq, a.ds, a.ts, a.count,    \
                                                             a.offset, a.active, a.n_active, a.H, \
-                                                            a.I, a.y)
+                                                            a.I, a.y, early)
 #define MOE_FEW_D_R(R_, F16_)                   \
   do {                                          \
     if (ks == 4) MOE_FEW_D(R_, 4, F16_);        \
