@@ -18,44 +18,74 @@ __device__ inline uint32_t load_u16(const uint8_t* p) {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// 8 values of one code dword dotted with 8 activations (4 pairs), accumulated into acc
-__device__ inline float dot8_bf16(uint32_t q, uint4 xx, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0),
-                                        __builtin_bit_cast(bf16x2_t, xx.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1),
-                                        __builtin_bit_cast(bf16x2_t, xx.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2),
-                                        __builtin_bit_cast(bf16x2_t, xx.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3),
-                                        __builtin_bit_cast(bf16x2_t, xx.w), acc, false);
-  return acc;
+// A lane's 32 weights decoded once (two 16-value scale blocks) and then dotted with any number
+// of activation rows: each block's dot times its e4m3 scale.
+struct Dec32bf {
+  bf16x2_t v[16];
+  float s0, s1;
+};
+struct Dec32h {
+  f16x2 v[16];
+  float s0, s1;
+};
+
+__device__ inline void decode32(uint4 q, uint32_t sbytes, Dec32bf& d) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d.v[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 0);
+    d.v[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 1);
+    d.v[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 2);
+    d.v[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, 3);
+  }
+  d.s0 = __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0);
+  d.s1 = __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
 }
 
-__device__ inline float dot8_f16(uint32_t q, uint4 xx, float acc) {
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0),
-                               __builtin_bit_cast(f16x2, xx.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1),
-                               __builtin_bit_cast(f16x2, xx.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2),
-                               __builtin_bit_cast(f16x2, xx.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3),
-                               __builtin_bit_cast(f16x2, xx.w), acc, false);
-  return acc;
+__device__ inline void decode32(uint4 q, uint32_t sbytes, Dec32h& d) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d.v[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0);
+    d.v[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1);
+    d.v[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2);
+    d.v[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3);
+  }
+  d.s0 = __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0);
+  d.s1 = __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
 }
 
-// A lane's 32 values (two 16-value scale blocks): each block's dot times its e4m3 scale.
-__device__ inline float dot32_bf16(uint4 q, uint32_t sbytes, const uint4* xv) {
-  const float b0 = dot8_bf16(q.y, xv[1], dot8_bf16(q.x, xv[0], 0.f));
-  const float b1 = dot8_bf16(q.w, xv[3], dot8_bf16(q.z, xv[2], 0.f));
-  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
-         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
+// xv: the 32 matching activations (four 16-byte pieces), in the order of the decoded values
+__device__ inline float dot32(const Dec32bf& d, const uint4* xv) {
+  float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t x0[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    const uint32_t x1[4] = {xv[i + 2].x, xv[i + 2].y, xv[i + 2].z, xv[i + 2].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0 = __builtin_amdgcn_fdot2_f32_bf16(d.v[4 * i + j], __builtin_bit_cast(bf16x2_t, x0[j]),
+                                           b0, false);
+      b1 = __builtin_amdgcn_fdot2_f32_bf16(d.v[8 + 4 * i + j],
+                                           __builtin_bit_cast(bf16x2_t, x1[j]), b1, false);
+    }
+  }
+  return b0 * d.s0 + b1 * d.s1;
 }
 
-__device__ inline float dot32_f16(uint4 q, uint32_t sbytes, const uint4* xv) {
-  const float b0 = dot8_f16(q.y, xv[1], dot8_f16(q.x, xv[0], 0.f));
-  const float b1 = dot8_f16(q.w, xv[3], dot8_f16(q.z, xv[2], 0.f));
-  return b0 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 0) +
-         b1 * __builtin_amdgcn_cvt_f32_fp8((int)sbytes, 1);
+__device__ inline float dot32(const Dec32h& d, const uint4* xv) {
+  float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t x0[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+    const uint32_t x1[4] = {xv[i + 2].x, xv[i + 2].y, xv[i + 2].z, xv[i + 2].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0 = __builtin_amdgcn_fdot2(d.v[4 * i + j], __builtin_bit_cast(f16x2, x0[j]), b0, false);
+      b1 = __builtin_amdgcn_fdot2(d.v[8 + 4 * i + j], __builtin_bit_cast(f16x2, x1[j]), b1, false);
+    }
+  }
+  return b0 * d.s0 + b1 * d.s1;
 }
 
 // the four K-groups of feature n (lanes n, n+16, n+32, n+48), fixed order

@@ -102,12 +102,15 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
     for (int u = 0; u < kSet; ++u) {
       const int c = c0 + u;
       if (c < nchunk) {
+        Dec32bf dg, du;  // decoded once, dotted with every row
+        decode32(qg[u], sg[u], dg);
+        decode32(qu[u], su[u], du);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (r < rows) {
             const uint4* xv = reinterpret_cast<const uint4*>(xs + (size_t)r * H + (cbeg + c) * kChunk + g * 32);
-            ag[r] += dot32_bf16(qg[u], sg[u], xv);
-            au[r] += dot32_bf16(qu[u], su[u], xv);
+            ag[r] += dot32(dg, xv);
+            au[r] += dot32(du, xv);
           }
         }
       }
@@ -211,10 +214,12 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
     for (int u = 0; u < kSet; ++u) {
       const int c = c0 + u;
       if (c < nchunk) {
+        Dec32h d;  // decoded once, dotted with every row
+        decode32(q[u], sc[u], d);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           if (r < rows)
-            acc[r] += dot32_f16(q[u], sc[u], reinterpret_cast<const uint4*>(hs + (size_t)r * I + (cbeg + c) * kChunk + g * 32));
+            acc[r] += dot32(d, reinterpret_cast<const uint4*>(hs + (size_t)r * I + (cbeg + c) * kChunk + g * 32));
       }
     }
   };

@@ -375,13 +375,16 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       for (int u = 0; u < kLsSetC; ++u) {
         const int c = cs + u;
         if (c < nch) {
+          Dec32bf dg, du;  // decoded once, dotted with every row
+          decode32(qg[u], sg[u], dg);
+          decode32(qu[u], su[u], du);
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
             if (r < rows) {
               const uint4* xv = reinterpret_cast<const uint4*>(
                   xs + (size_t)srow_tok[off + r] * H + c * kChunk + g * 32);
-              ag[r] += dot32_bf16(qg[u], sg[u], xv);
-              au[r] += dot32_bf16(qu[u], su[u], xv);
+              ag[r] += dot32(dg, xv);
+              au[r] += dot32(du, xv);
             }
           }
         }
@@ -476,12 +479,14 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         for (int u = 0; u < kLsSetD; ++u) {
           const int c = cs + u;
           if (c < nck) {
+            Dec32h d;  // decoded once, dotted with every row
+            decode32(q[u], sc[u], d);
 #pragma unroll
             for (int r = 0; r < TT; ++r) {
               if (r < rows) {
                 const uint4* hv = reinterpret_cast<const uint4*>(
                     hs + ((size_t)kh * nq + off + r) * hw_row + c * (kChunk / 2) + g * 16);
-                racc[r] += dot32_f16(q[u], sc[u], hv);
+                racc[r] += dot32(d, hv);
               }
             }
           }
