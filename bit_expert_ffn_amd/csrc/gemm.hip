@@ -23,6 +23,7 @@ constexpr int gK = 64;       // K per pipeline stage
 constexpr int gLD = gK + 8;  // padded LDS row, in halves
 constexpr int kXcds = 8;     // MI355X: 8 accelerator dies (XCDs), workgroups dealt round-robin
 constexpr int kGroup = 4;    // consecutive row tiles whose blocks are ordered together
+constexpr int kGemmSets = 4;  // register sets of the load pipeline
 
 __device__ inline f16x8 gdecode8(uint32_t q, f16x2 s) {
   const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * s;
@@ -85,12 +86,13 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     ffn_plan(count, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
-// Block: 256 threads = 4 wavefronts side by side in N; MT = 64 * WM rows x 256 weight rows; K
-// in stages of 64.  Every wavefront computes all MT rows (MI = MT / 32 tiles of 32) against its
-// own 2 weight tiles of 32 rows:
-//   gate/up: wavefront wn takes features f0 + 32 wn .. + 31 of the block's 128: its gate tile
+// Block: NW wavefronts side by side in N; MT = 64 * WM rows x 64 NW weight rows; K in stages of
+// 64.  Every wavefront computes all MT rows (MI = MT / 32 tiles of 32) against its own 2 weight
+// tiles of 32 rows:
+//   gate/up: wavefront wn takes features f0 + 32 wn .. + 31 of the block's 32 NW: its gate tile
 //            and the up tile of the same features; h = silu(g) * u in the epilogue;
-//   down:    rows n0 + 64 wn + {0, 32} -> 256 output features per block.
+//   down:    rows n0 + 64 wn + {0, 32} -> 64 NW output features per block.
+// Wider blocks read each activation tile fewer times (once per block of weight rows).
 // Each weight byte is loaded and decoded by one wavefront only, and each decoded fragment feeds
 // MI MFMAs.  Activations go through LDS (double buffered, rows padded to 144 bytes) and every
 // wavefront reads all of them.  Weights do not: each lane loads, per stage and per weight
@@ -100,17 +102,19 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
 // K may be permuted: step i takes codes 8i..8i+7 of the lane's group, and the activation
 // operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
 // loads of activations and packed weights run ahead in S register sets.
-template <bool GATEUP, int WM, bool Y_F16, int S>
-__global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
+template <bool GATEUP, int WM, bool Y_F16, int S, int NW>
+__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ sorted_slot, const int2* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out) {
+  constexpr int NTH = 64 * NW;      // threads per block
   constexpr int MT = 64 * WM;
-  constexpr int MI = MT / 32;  // 32-row tiles per wavefront
-  constexpr int NA = MT / 32;  // 16-byte activation pieces per thread per stage
+  constexpr int MI = MT / 32;        // 32-row tiles per wavefront
+  constexpr int NA = MT * 8 / NTH;   // 16-byte activation pieces per thread per stage
+  static_assert(NA >= 1, "block tile too small for its threads");
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native vector: stays in VGPRs
   __shared__ __attribute__((aligned(16))) _Float16 As[2][MT][gLD];
   // Block order.  Workgroups go round-robin to the 8 XCDs, each with its own L2; renumber so
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   uint32_t aoff[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int sidx = tid + 256 * i;
+    const int sidx = tid + NTH * i;
     const int r = min(m0 + (sidx >> 3), rows - 1);
     const uint32_t src = GATEUP ? (uint32_t)(sorted_slot[base + r] / k) * (uint32_t)H
                                 : (uint32_t)(base + r) * (uint32_t)I;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
   int feat[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = GATEUP ? fb * 128 + wn * 32 + r32 : fb * 256 + wn * 64 + t * 32 + r32;
+    const int row = GATEUP ? fb * (32 * NW) + wn * 32 + r32 : fb * (64 * NW) + wn * 64 + t * 32 + r32;
     feat[t] = row;
     const int rc = min(row, N - 1);
     const uint32_t tile0 = (uint32_t)(rc >> 4) * (uint32_t)nchunk;
@@ -205,11 +209,11 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
     r.s1 = *reinterpret_cast<const uint32_t*>(sbt1 + ((soff[1] + cs) & ~3u));
   };
   auto store_a = [&](const Stage& r, int buf) __attribute__((always_inline)) {
-    // piece i of this thread: s = tid + 256 * i -> row s >> 3, 16-byte column s & 7
+    // piece i of this thread: s = tid + NTH * i -> row s >> 3, 16-byte column s & 7
     const int c8 = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + 32 * i][c8]) = r.a[i];
+      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + (NTH / 8) * i][c8]) = r.a[i];
   };
 
   f32x16 acc[MI][2];
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
-        if (m < rows) {
+        if (m < rows && f < I) {
           const float gv = acc[i][0][v] * tsg, uv = acc[i][1][v] * tsu;
           h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
         }
@@ -327,26 +331,27 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
   const size_t n8 = (size_t)a.T * a.H / 8;
   x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
       a.x, a.x16, n8, a.count, a.active, a.n_active, MT, min_rows, tiles, max_tiles, n_tiles);
-  const dim3 gg(a.I / 128, max_tiles), gd((a.H + 255) / 256, max_tiles);
-#define MOE_GEMM_S(GU_, WM_, F16_, S_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                  \
-  ffn_gemm_kernel<GU_, WM_, F16_, S_><<<GRID_, 256, 0, s>>>(XA_, Q0_, S0_, Q1_, S1_, a.ts,      \
-                                                            a.count, a.offset, a.sorted_slot,   \
-                                                            tiles, n_tiles, a.k, a.H, a.I, OUT_)
-  // 64-row tiles: four register sets; 128-row tiles: three, which still leaves room for two
-  // wavefronts per SIMD
-#define MOE_GEMM(GU_, WM_, F16_, GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
-  MOE_GEMM_S(GU_, WM_, F16_, (WM_ == 1 ? 4 : 3), GRID_, XA_, Q0_, S0_, Q1_, S1_, OUT_)
+  // 128-row tiles: 8 wavefronts (512 weight rows per block); 64-row tiles (fewer rows, fewer
+  // blocks): 4 wavefronts
+#define MOE_GEMM(GU_, WM_, F16_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
+  do {                                                                                        \
+    constexpr int NW_ = WM_ == 2 ? 8 : 4;                                                     \
+    const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
+                  max_tiles);                                                                 \
+    ffn_gemm_kernel<GU_, WM_, F16_, kGemmSets, NW_><<<g_, 64 * NW_, 0, s>>>(                  \
+        XA_, Q0_, S0_, Q1_, S1_, a.ts, a.count, a.offset, a.sorted_slot, tiles, n_tiles, a.k,  \
+        a.H, a.I, OUT_);                                                                      \
+  } while (0)
   if (MT == 128) {
-    MOE_GEMM(true, 2, false, gg, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 2, true, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 2, false, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    MOE_GEMM(true, 2, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16) MOE_GEMM(false, 2, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else MOE_GEMM(false, 2, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
   } else {
-    MOE_GEMM(true, 1, false, gg, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 1, true, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 1, false, gd, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    MOE_GEMM(true, 1, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16) MOE_GEMM(false, 1, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else MOE_GEMM(false, 1, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
   }
 #undef MOE_GEMM
-#undef MOE_GEMM_S
   return hipGetLastError();
 }
 
