@@ -199,6 +199,33 @@ def combine(y, slot_row, topk_w, k, H):
     return out
 
 
+def combine_norm(y, slot_row, topk_w, k, H, expert_norm=False, resid=None, alpha=1.0,
+                 beta=1.0, gain=None, eps=1e-6):
+    """Combine variants in fp64: per-expert RMS norm before the weighted sum (expert_norm) and,
+    when resid is given, the post-norm + scaled residual + next pre-norm epilogue.  Returns a
+    dict: f (the combined MoE output), out (new residual, or f without the epilogue) and, with
+    the epilogue, s and r (per-token norm factors) and xn (the next layer's input, unrounded)."""
+    y = _c(y, np.float64)
+    slot_row = _c(slot_row, np.int32)
+    topk_w = _c(topk_w, np.float64)
+    T = topk_w.shape[0]
+    epi = resid is not None
+    f = np.empty((T, H), np.float64)
+    out = np.empty((T, H), np.float64)
+    res = dict(f=f, out=out)
+    args = [None] * 5
+    if epi:
+        resid = _c(resid, np.float64)
+        gain = _c(gain, np.float64)
+        res.update(s=np.empty(T), r=np.empty(T), xn=np.empty((T, H)))
+        args = [resid, gain, res["s"], res["r"], res["xn"]]
+    _load().oracle_combine_norm(
+        _p(y), _p(slot_row), _p(topk_w), T, k, H, int(expert_norm), int(epi),
+        ctypes.c_double(eps), _p(args[0]), ctypes.c_double(alpha), ctypes.c_double(beta),
+        _p(args[1]), _p(f), _p(args[2]), _p(out), _p(args[3]), _p(args[4]))
+    return res
+
+
 def layer(x_bits, w_router, bias, experts, k):
     """Whole layer on every token: dict of logits, topk ids/weights, grouping, y, out."""
     logits = router(x_bits, w_router, bias)

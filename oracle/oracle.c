@@ -196,6 +196,53 @@ void oracle_combine(const double *y, const int32_t *slot_row, const double *topk
     }
 }
 
+/* Root-mean-square norm factor of one row: 1 / sqrt(mean(v^2) + eps) (Zhang and Sennrich,
+ * "Root Mean Square Layer Normalization", the RMS norm the Muse Spark page cites). */
+static double rms_factor(const double *v, int H, double eps) {
+  double ss = 0.0;
+  for (int n = 0; n < H; ++n) ss += v[n] * v[n];
+  return 1.0 / sqrt(ss / H + eps);
+}
+
+/* Combine variants ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", section 8 "A
+ * one-pass combine" and "The fused MoE kernel and the pair exchange"; section 3, the residual
+ * stream of "What makes this possible is where Muse Spark normalizes"; "A 501B sparse model
+ * gets day-one serving support": post-norm, scaled residual and next pre-norm in one kernel).
+ *   expert_norm: each expert row is RMS-normalised (no gain) before the weighted sum:
+ *       f[t] = sum over j ascending of w[t][j] * rms_factor(y_j) * y_j,   y_j = y[slot_row[t*k+j]]
+ *     otherwise f[t] is the plain weighted sum.
+ *   epilogue: s = rms_factor(f[t]) (the MoE output's own norm factor),
+ *       out[t]  = alpha * resid[t] + beta * s * f[t]          (the new residual stream)
+ *       r       = rms_factor(out[t])
+ *       xn[t]   = gain * out[t] * r                            (the next layer's input)
+ *     otherwise out[t] = f[t] and s, r, xn are not written.
+ * f, out, xn are [T][H]; s and r are [T] (may be NULL). */
+void oracle_combine_norm(const double *y, const int32_t *slot_row, const double *topk_w, int T,
+                         int k, int H, int expert_norm, int epilogue, double eps,
+                         const double *resid, double alpha, double beta, const double *gain,
+                         double *f, double *s, double *out, double *r, double *xn) {
+  for (int t = 0; t < T; ++t) {
+    double *ft = f + (size_t)t * H;
+    for (int n = 0; n < H; ++n) ft[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const double *yj = y + (size_t)slot_row[t * k + j] * H;
+      const double c = topk_w[(size_t)t * k + j] * (expert_norm ? rms_factor(yj, H, eps) : 1.0);
+      for (int n = 0; n < H; ++n) ft[n] += c * yj[n];
+    }
+    double *ot = out + (size_t)t * H;
+    if (!epilogue) {
+      for (int n = 0; n < H; ++n) ot[n] = ft[n];
+      continue;
+    }
+    const double st = rms_factor(ft, H, eps);
+    for (int n = 0; n < H; ++n) ot[n] = alpha * resid[(size_t)t * H + n] + beta * st * ft[n];
+    const double rt = rms_factor(ot, H, eps);
+    for (int n = 0; n < H; ++n) xn[(size_t)t * H + n] = gain[n] * ot[n] * rt;
+    if (s) s[t] = st;
+    if (r) r[t] = rt;
+  }
+}
+
 void oracle_layer_tokens(const uint16_t *x, const float *w_router, const float *bias,
                          const oracle_experts *w, int H, int E, int k, const int32_t *tokens,
                          int ntok, float *logits, int32_t *topk_id, double *topk_w, double *out) {

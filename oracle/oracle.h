@@ -69,6 +69,12 @@ void oracle_expert_hidden(const uint16_t *x, int H, const oracle_experts *w, int
                           const int32_t *tok, int nrows, double *h);
 void oracle_combine(const double *y, const int32_t *slot_row, const double *topk_w,
                     int T, int k, int H, double *out);
+/* Combine variants: per-expert RMS norm before the weighted sum (expert_norm) and the
+ * post-norm + scaled residual + next pre-norm epilogue (epilogue); definitions in oracle.c. */
+void oracle_combine_norm(const double *y, const int32_t *slot_row, const double *topk_w, int T,
+                         int k, int H, int expert_norm, int epilogue, double eps,
+                         const double *resid, double alpha, double beta, const double *gain,
+                         double *f, double *s, double *out, double *r, double *xn);
 /* The whole layer for the listed tokens only (routing is per token, so any subset is exact).
  * ids/w/logits/out are [ntok][k], [ntok][k], [ntok][E], [ntok][H]. */
 void oracle_layer_tokens(const uint16_t *x, const float *w_router, const float *bias,

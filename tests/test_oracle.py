@@ -372,3 +372,147 @@ def test_planted_transpose_is_caught_by_dense_pin():
     good = oracle.expert_rows(N["x"], ex, 0, np.arange(sp["T"]))
     bad = (_silu(x @ Wg.T) * (x @ Wu.T)) @ Wd  # transposed down weights
     assert not np.allclose(good, bad, rtol=1e-3)
+
+
+# ---------------------------------------------------------------- combine variants
+def _golden_kv(name):
+    return {r[0]: np.array([float(v) for v in r[1:]]) for r in _read_table(name)}
+
+
+def test_combine_norm_hand_example():
+    """Hand-worked example (tests/golden/combine_norm_example.txt): per-expert norm, plain
+    weighted sum, and the post-norm + scaled residual + next pre-norm epilogue."""
+    g = _golden_kv("combine_norm_example.txt")
+    y = np.stack([g["y0"], g["y1"]])
+    slot_row = g["slot_row"].astype(np.int32)
+    w = g["topk_w"][None, :]
+    plain = oracle.combine_norm(y, slot_row, w, 2, 4, eps=0.0)
+    assert np.allclose(plain["out"][0], g["f_plain"], rtol=0, atol=1e-15)
+    normed = oracle.combine_norm(y, slot_row, w, 2, 4, expert_norm=True, eps=0.0)
+    assert np.allclose(normed["out"][0], g["f"], rtol=0, atol=1e-15)
+    epi = oracle.combine_norm(y, slot_row, w, 2, 4, expert_norm=True, resid=g["resid"][None, :],
+                              alpha=float(g["alpha"][0]), beta=float(g["beta"][0]),
+                              gain=g["gain"], eps=0.0)
+    assert np.allclose(epi["f"][0], g["f"], rtol=0, atol=1e-15)
+    assert abs(epi["s"][0] - g["s"][0]) < 1e-13
+    assert np.allclose(epi["out"][0], g["out"], rtol=0, atol=1e-13)
+    assert abs(epi["r"][0] - g["r"][0]) < 1e-15
+    assert np.allclose(epi["xn"][0], g["xn"], rtol=0, atol=1e-14)
+
+
+def test_combine_norm_epsilon_closed_form():
+    """One expert row of constant value c: mean square c^2, factor 1/sqrt(c^2 + eps)."""
+    H = 8
+    y = np.full((1, H), 2.0)
+    out = oracle.combine_norm(y, np.array([0], np.int32), np.array([[0.5]]), 1, H,
+                              expert_norm=True, eps=5.0)["out"]
+    assert np.allclose(out, 0.5 * 2.0 / 3.0, rtol=1e-15)
+
+
+def test_combine_norm_flags_off_is_weighted_sum():
+    """Without the per-expert norm and the epilogue the variant is the plain routing-weighted
+    sum: numpy's einsum over the gathered rows."""
+    T, k, H = 5, 3, 24
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal((T * k, H))
+    slot_row = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k))
+    got = oracle.combine_norm(y, slot_row, w, k, H)["out"]
+    want = np.einsum("tj,tjh->th", w, y[slot_row].reshape(T, k, H))
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+def test_combine_expert_norm_is_scale_invariant_per_expert():
+    """With eps = 0 each expert's row is normalised before weighting: scaling one expert row by
+    a positive factor leaves f unchanged, a negative one flips that expert's contribution.  A
+    norm applied after the sum (or to the wrong rows) fails this."""
+    T, k, H = 4, 3, 32
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((T * k, H))
+    slot_row = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k))
+    base = oracle.combine_norm(y, slot_row, w, k, H, expert_norm=True, eps=0.0)["out"]
+    y2 = y * rng.uniform(0.01, 100.0, (T * k, 1))
+    same = oracle.combine_norm(y2, slot_row, w, k, H, expert_norm=True, eps=0.0)["out"]
+    assert np.allclose(same, base, rtol=1e-12, atol=1e-13)
+    t, j = 2, 1
+    y3 = y.copy()
+    y3[slot_row[t * k + j]] *= -7.0
+    flip = oracle.combine_norm(y3, slot_row, w, k, H, expert_norm=True, eps=0.0)["out"]
+    row = y[slot_row[t * k + j]]
+    contrib = w[t, j] * row / np.sqrt(np.mean(row * row))
+    assert np.allclose(flip[t], base[t] - 2 * contrib, rtol=1e-12, atol=1e-13)
+    # k = 1, weight 1: the output row has root-mean-square exactly 1
+    one = oracle.combine_norm(y[:T], np.arange(T, dtype=np.int32), np.ones((T, 1)), 1, H,
+                              expert_norm=True, eps=0.0)["out"]
+    assert np.allclose(np.sqrt(np.mean(one * one, axis=1)), 1.0, rtol=1e-14)
+
+
+def test_combine_norm_after_sum_is_caught():
+    """Planted mistake on the CPU: normalising the weighted sum instead of each expert row must
+    differ from the oracle on rows of unequal scale."""
+    T, k, H = 3, 4, 16
+    rng = np.random.default_rng(23)
+    y = rng.standard_normal((T * k, H)) * rng.uniform(0.1, 10.0, (T * k, 1))
+    slot_row = np.arange(T * k, dtype=np.int32)
+    w = rng.random((T, k))
+    good = oracle.combine_norm(y, slot_row, w, k, H, expert_norm=True, eps=0.0)["out"]
+    s = np.einsum("tj,tjh->th", w, y.reshape(T, k, H))
+    bad = s / np.sqrt(np.mean(s * s, axis=1, keepdims=True))
+    assert not np.allclose(good, bad, rtol=1e-3)
+
+
+def test_combine_norm_epilogue_special_cases():
+    """beta = 0, alpha = 1: the new residual is the old one and the next input is torch's RMS
+    norm of it with the gain.  alpha = 0: the new residual is beta times the RMS-normalised MoE
+    output (root-mean-square |beta|).  Scaling alpha and beta together scales the residual and
+    leaves the next input unchanged (eps = 0)."""
+    T, k, H = 6, 2, 40
+    rng = np.random.default_rng(24)
+    y = rng.standard_normal((T * k, H))
+    slot_row = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k))
+    resid = rng.standard_normal((T, H)) * 3.0
+    gain = rng.uniform(0.5, 1.5, H)
+    eps = 1e-6
+    a = oracle.combine_norm(y, slot_row, w, k, H, resid=resid, alpha=1.0, beta=0.0, gain=gain,
+                            eps=eps)
+    assert np.array_equal(a["out"], resid)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(resid), (H,),
+                                        weight=torch.from_numpy(gain), eps=eps).numpy()
+    assert np.allclose(a["xn"], want, rtol=1e-12, atol=1e-14)
+    b = oracle.combine_norm(y, slot_row, w, k, H, expert_norm=True, resid=resid, alpha=0.0,
+                            beta=-2.5, gain=gain, eps=0.0)
+    assert np.allclose(np.sqrt(np.mean(b["out"] ** 2, axis=1)), 2.5, rtol=1e-13)
+    f = b["f"]
+    assert np.allclose(b["xn"], -gain * f / np.sqrt(np.mean(f * f, axis=1, keepdims=True)),
+                       rtol=1e-12, atol=1e-14)
+    c1 = oracle.combine_norm(y, slot_row, w, k, H, resid=resid, alpha=0.7, beta=1.3, gain=gain,
+                             eps=0.0)
+    c2 = oracle.combine_norm(y, slot_row, w, k, H, resid=resid, alpha=0.7 * 4, beta=1.3 * 4,
+                             gain=gain, eps=0.0)
+    assert np.allclose(c2["out"], 4 * c1["out"], rtol=1e-13, atol=1e-13)
+    assert np.allclose(c2["xn"], c1["xn"], rtol=1e-12, atol=1e-14)
+
+
+def test_combine_norm_chain_matches_torch_rms_norm():
+    """The whole variant composed from torch's RMS norm (float64, CPU): per-row norm of each
+    expert output, weighted sum, norm factor of the sum, scaled residual, norm with gain."""
+    T, k, H = 5, 4, 48
+    rng = np.random.default_rng(25)
+    y = rng.standard_normal((T * k, H))
+    slot_row = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k))
+    resid = rng.standard_normal((T, H))
+    gain = rng.uniform(0.5, 1.5, H)
+    eps, alpha, beta = 1e-5, 0.9, 1.7
+    got = oracle.combine_norm(y, slot_row, w, k, H, expert_norm=True, resid=resid, alpha=alpha,
+                              beta=beta, gain=gain, eps=eps)
+    rms = torch.nn.functional.rms_norm
+    yt = rms(torch.from_numpy(y[slot_row]).reshape(T, k, H), (H,), eps=eps)
+    f = (torch.from_numpy(w)[:, :, None] * yt).sum(1)
+    out = alpha * torch.from_numpy(resid) + beta * rms(f, (H,), eps=eps)
+    xn = rms(out, (H,), weight=torch.from_numpy(gain), eps=eps)
+    assert np.allclose(got["f"], f.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.allclose(got["out"], out.numpy(), rtol=1e-12, atol=1e-14)
+    assert np.allclose(got["xn"], xn.numpy(), rtol=1e-12, atol=1e-14)
