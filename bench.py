@@ -9,6 +9,10 @@ single-launch kernel, or the expert-FFN call of the four-call path); its HBM tra
 committed PMC summary when the kernel is unchanged since; and the CPU oracle timed on a
 bounded sample.
 
+--combine norm replaces the plain combine with the combine variants (per-expert RMS norm before
+the weighted sum, then the residual update and the next layer's RMS norm) and runs the four-call
+path at every T; the combine call is timed with its own HIP events in both modes.
+
 Workloads (hidden 7168, 256 experts, top-8, NVFP4 experts):
   decode1     T=1, expert intermediate 2048; each step takes the next token of a seeded pool of
               64 tokens, so consecutive steps read different experts (as decoding does) rather
@@ -47,6 +51,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode1",
                     choices=["decode1", "decode64", "verify128", "prefill16k"])
+    ap.add_argument("--combine", default="plain", choices=["plain", "norm"],
+                    help="plain: routing-weighted sum; norm: per-expert RMS norm before the sum "
+                         "and the residual + next pre-norm epilogue (four-call path)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle sample budget (0 disables the CPU baseline)")
     args = ap.parse_args()
@@ -82,11 +89,19 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    fused = T <= 2  # one or two tokens: the whole layer is one persistent kernel
+    # one or two tokens: the whole layer is one persistent kernel (plain combine only)
+    fused = T <= 2 and args.combine == "plain"
+    norm = args.combine == "norm"
+    if norm:
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        resid = torch.randn((T, H), generator=g, device=dev, dtype=torch.float32)
+        gain = torch.rand((H,), generator=g, device=dev, dtype=torch.float32) + 0.5
+        x_next = torch.empty((T, H), device=dev, dtype=torch.bfloat16)
     calls = ([moe.prepare_layer_nvfp4(x_of(i), wr, bias, ex, k, buf, stream=stream)
               for i in range(pool)] if fused else None)
 
-    def step(i, ev=None):
+    def step(i, ev=None, evc=None):
         x = x_of(i)
         if fused:
             if ev is not None:
@@ -104,7 +119,16 @@ def main():
                              buf.n_active, k, buf.y, buf.ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        moe.combine(buf.y, buf.slot_row, buf.topk_w, buf.out, stream=stream)
+        if evc is not None:
+            evc[0].record(stream)
+        if norm:  # the residual stream is updated in place
+            moe.combine_norm(buf.y, buf.slot_row, buf.topk_w, resid, expert_norm=True,
+                             resid=resid, alpha=1.0, beta=1.0, gain=gain, x_next=x_next,
+                             stream=stream)
+        else:
+            moe.combine(buf.y, buf.slot_row, buf.topk_w, buf.out, stream=stream)
+        if evc is not None:
+            evc[1].record(stream)
 
     for i in range(warmup):
         step(i)
@@ -116,13 +140,15 @@ def main():
     # path), or around the whole run when a step is the single-launch kernel
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
+    evcs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
     ev_all = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     n_distinct = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev_all[0].record(stream)
     for i in range(steps):
-        step(warmup + i, None if fused else evs[i])
+        step(warmup + i, None if fused else evs[i], None if fused else evcs[i])
     ev_all[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -130,6 +156,7 @@ def main():
         ffn_ms = ev_all[0].elapsed_time(ev_all[1]) / steps
     else:
         ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        comb_ms = sum(a.elapsed_time(b) for a, b in evcs) / steps
 
     # distinct experts touched per step (re-run routing+grouping outside the timed region)
     for i in range(min(steps, POOL if T == 1 else 1)):
@@ -164,9 +191,22 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel)
 
+    combine = None
+    if not fused:
+        # y (f16) + slot_row + weights per token; plain: out fp32; norm: resid fp32 read,
+        # new residual fp32 written, x_next bf16 written (gain [H] fp32 read once)
+        cb = T * (k * H * 2 + k * 8) + (T * H * 10 + H * 4 if norm else T * H * 4)
+        combine = dict(kernel="combine_norm_kernel" if norm else "combine_kernel",
+                       variant="expert_norm+residual_norm" if norm else "plain",
+                       us=round(comb_ms * 1e3, 2), algorithmic_bytes=int(cb),
+                       achieved_gbs=round(cb / (comb_ms * 1e-3) / 1e9, 1),
+                       frac=round(cb / (comb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(layer, sp, pool, args.cpu_seconds)
+        if norm:
+            cpu["combine_norm"] = cpu_combine_norm(T, k, H, min(T, 256))
 
     res = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
@@ -174,6 +214,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": wl, "T": T, "H": H, "I": I, "E": E, "k": k,
+                   "combine": "expert_norm+residual_norm" if norm else "plain",
                    "weights": "nvfp4 (e2m1, e4m3 per 16, fp32 per matrix)",
                    "token_pool": pool, "seed": 0, "parallelism": "none (1 GPU)"},
         "roofline": roof,
@@ -183,6 +224,7 @@ def main():
         "distinct_experts": round(nd, 2),
         "layer_hbm_frac": round(layer_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_algorithmic_bytes": int(kbytes),
+        "combine": combine,
         "ffn_flops": flops,
     }
     print(json.dumps(res))
@@ -233,6 +275,20 @@ def cpu_baseline(layer, sp, pool, budget_s):
             "kind": "oracle",
             "sample": "%d token(s) of the %s workload, whole layer per token (fp64 oracle)"
                       % (done, "decode" if pool > 1 else "same")}
+
+
+def cpu_combine_norm(T, k, H, ntok):
+    """The oracle's combine variants (per-expert norm + epilogue) on ntok tokens of seeded
+    inputs of the workload's shape, tokens/s."""
+    import oracle
+    import synth
+    d = {n: v.numpy() for n, v in synth.make_combine_inputs(ntok, k, H, seed=12).items()}
+    t0 = time.perf_counter()
+    oracle.combine_norm(d["y"].astype("float32"), d["slot_row"], d["topk_w"], k, H,
+                        expert_norm=True, resid=d["resid"], gain=d["gain"])
+    dt = time.perf_counter() - t0
+    return {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": 1,
+            "sample": "%d tokens, per-expert norm + residual + next pre-norm (fp64 oracle)" % ntok}
 
 
 if __name__ == "__main__":

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 MOE_F32 = 0
 MOE_F16 = 1
+MOE_COMBINE_EXPERT_NORM = 1
+MOE_COMBINE_RESIDUAL_NORM = 2
 _lib = None
 
 
@@ -51,6 +53,10 @@ def lib():
                                            i32, i32, vp, i32, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_combine_norm.restype = i32
+        L.moe_combine_norm.argtypes = [vp, i32, vp, vp, i32, i32, i32, ctypes.c_uint32,
+                                       ctypes.c_float, vp, ctypes.c_float, ctypes.c_float, vp,
+                                       vp, vp, vp]
         L.moe_nvfp4_pack.restype = i32
         L.moe_nvfp4_pack.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
         L.moe_layer_nvfp4.restype = i32
@@ -61,8 +67,8 @@ def lib():
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
-            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_nvfp4_pack",
-            "moe_layer_nvfp4")
+            "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_norm",
+            "moe_nvfp4_pack", "moe_layer_nvfp4")
 
 
 def abi_version():
@@ -203,6 +209,27 @@ def combine(y, slot_row, topk_w, out, stream=None):
             _dev(topk_w, "topk_w", torch.float32, (T, k)), T, k, H,
             _dev(out, "out", torch.float32, (T, H)), _stream(stream, y.device))
     _check(lib().moe_combine(*args), "moe_combine")
+
+
+def combine_norm(y, slot_row, topk_w, out, expert_norm=False, resid=None, alpha=1.0, beta=1.0,
+                 gain=None, x_next=None, eps=1e-6, stream=None):
+    """moe_combine_norm: the weighted sum with a per-expert RMS norm of each expert row
+    (expert_norm) and, when resid is given, the epilogue out = alpha * resid + beta * s * f with
+    s = f's RMS factor, x_next [T][H] bf16 = gain * RMS-norm(out).  resid may be out itself."""
+    T, k = topk_w.shape
+    H = y.shape[1]
+    yd = MOE_F16 if y.dtype == torch.float16 else MOE_F32
+    flags = MOE_COMBINE_EXPERT_NORM if expert_norm else 0
+    epi = (None, None, None)
+    if resid is not None:
+        flags |= MOE_COMBINE_RESIDUAL_NORM
+        epi = (_dev(resid, "resid", torch.float32, (T, H)), _dev(gain, "gain", torch.float32, (H,)),
+               _dev(x_next, "x_next", torch.bfloat16, (T, H)))
+    args = (_dev(y, "y", y.dtype, (T * k, H)), yd, _dev(slot_row, "slot_row", torch.int32, (T * k,)),
+            _dev(topk_w, "topk_w", torch.float32, (T, k)), T, k, H, flags, float(eps), epi[0],
+            float(alpha), float(beta), epi[1], _dev(out, "out", torch.float32, (T, H)), epi[2],
+            _stream(stream, y.device))
+    _check(lib().moe_combine_norm(*args), "moe_combine_norm")
 
 
 class LayerBuffers:

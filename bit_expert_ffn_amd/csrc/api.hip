@@ -176,6 +176,36 @@ MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t
                                       H, out_dev, (hipStream_t)stream));
 }
 
+MOE_API moe_status moe_combine_norm(const void* y_dev, int32_t y_dtype,
+                                    const int32_t* slot_row_dev, const float* topk_w_dev,
+                                    int32_t T, int32_t k, int32_t H, uint32_t flags, float eps,
+                                    const float* resid_dev, float alpha, float beta,
+                                    const float* gain_dev, float* out_dev, uint16_t* x_next_dev,
+                                    void* stream) {
+  if (!y_dev || !slot_row_dev || !topk_w_dev || !out_dev) return MOE_ERR_INVALID_ARGUMENT;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_F16) return MOE_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(MOE_COMBINE_EXPERT_NORM | MOE_COMBINE_RESIDUAL_NORM))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOE_ERR_INVALID_ARGUMENT;
+  const bool epi = (flags & MOE_COMBINE_RESIDUAL_NORM) != 0;
+  if (epi && (!resid_dev || !gain_dev || !x_next_dev)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_dev) || !aligned16(slot_row_dev) || !aligned16(topk_w_dev) ||
+      !aligned16(out_dev))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (epi && (!aligned16(resid_dev) || !aligned16(gain_dev) || !aligned16(x_next_dev)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, H, 128, k, k);
+  if (st != MOE_OK) return st;
+  moe::CombineNormArgs a;
+  a.y = y_dev; a.slot_row = slot_row_dev; a.w = topk_w_dev;
+  a.T = T; a.k = k; a.H = H;
+  a.expert_norm = (flags & MOE_COMBINE_EXPERT_NORM) != 0;
+  a.epilogue = epi;
+  a.eps = eps; a.alpha = alpha; a.beta = beta;
+  a.resid = resid_dev; a.gain = gain_dev; a.out = out_dev; a.x_next = x_next_dev;
+  return from_hip(moe::launch_combine_norm(a, y_dtype == MOE_F16, (hipStream_t)stream));
+}
+
 MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
                                    const float* bias_dev, const moe_nvfp4_experts* w, int32_t T,
                                    int32_t k, float* logits_dev, int32_t* topk_id_dev,

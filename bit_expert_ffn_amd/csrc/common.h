@@ -103,6 +103,22 @@ hipError_t launch_pack(const uint8_t* q_in, const uint8_t* s_in, int E, int N, i
 hipError_t launch_combine(const void* y, int y_f16, const int32_t* slot_row, const float* w,
                           int T, int k, int H, float* out, hipStream_t s);
 
+// Combine variants (per-expert RMS norm before the weighted sum; post-norm + scaled residual +
+// next pre-norm epilogue).  resid and out may be the same array.
+struct CombineNormArgs {
+  const void* y;          // [rows][H] f16 or fp32, grouped row order
+  const int32_t* slot_row;
+  const float* w;         // [T][k]
+  int T, k, H;
+  int expert_norm, epilogue;
+  float eps, alpha, beta;
+  const float* resid;     // [T][H] (epilogue)
+  const float* gain;      // [H] (epilogue)
+  float* out;             // [T][H]
+  uint16_t* x_next;       // [T][H] bf16 (epilogue)
+};
+hipError_t launch_combine_norm(const CombineNormArgs& a, int y_f16, hipStream_t s);
+
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also releases global memory, which

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 2
+#define MOE_NVFP4_ABI_VERSION 3
 
 typedef int32_t moe_status;
 enum {
@@ -169,6 +169,43 @@ moe_status moe_nvfp4_pack(const uint8_t *q_rowmajor_dev, const uint8_t *s_rowmaj
 moe_status moe_combine(const void *y_dev, int32_t y_dtype, const int32_t *slot_row_dev,
                        const float *topk_w_dev, int32_t T, int32_t k, int32_t H, float *out_dev,
                        void *stream);
+
+/* Combine variants: the weighted sum of moe_combine with one or both of
+ *   MOE_COMBINE_EXPERT_NORM: every expert output row is RMS-normalised (no gain) before it is
+ *     weighted ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", section 8, "The
+ *     fused MoE kernel and the pair exchange": each expert's output is normalised before the
+ *     weighted sum; "A one-pass combine": norm and weighted sum in one pass over the rows):
+ *         f[t] = sum over j of topk_w[t][j] * y_j / sqrt(mean(y_j^2) + eps),
+ *         y_j = y[slot_row[t*k+j]]; without the flag f[t] is moe_combine's sum;
+ *   MOE_COMBINE_RESIDUAL_NORM: the epilogue that follows the MoE output in the residual stream
+ *     (same page, section 3, "What makes this possible is where Muse Spark normalizes": the next
+ *     layer's input is an RMS norm of alpha * x + beta * s * f, s being f's own RMS factor;
+ *     "A 501B sparse model gets day-one serving support": post-norm, scaled residual and next
+ *     pre-norm fused in one kernel):
+ *         s = 1 / sqrt(mean(f[t]^2) + eps)
+ *         out[t] = alpha * resid[t] + beta * s * f[t]                  (fp32, new residual)
+ *         x_next[t] = bf16(gain * out[t] / sqrt(mean(out[t]^2) + eps))  (round to nearest even)
+ *     Without the flag out[t] = f[t]; resid, gain and x_next are not read or written and may be
+ *     NULL.
+ * RMS norm as defined by Zhang and Sennrich, "Root Mean Square Layer Normalization" (the norm
+ * the Muse Spark page cites).  The readings taken where the pages are silent: the per-expert
+ * norm and the post-norm have no gain, the one eps serves all three norms, alpha and beta are
+ * scalars.
+ * Shapes: y_dev [T*k][H] of y_dtype (grouped rows, as written by moe_expert_ffn_nvfp4),
+ * slot_row_dev [T*k], topk_w_dev [T][k] fp32, resid_dev and out_dev [T][H] fp32, gain_dev [H]
+ * fp32, x_next_dev [T][H] bf16 (the input format of the next layer's moe_route).  resid_dev may
+ * equal out_dev (update in place); no other overlap between inputs and outputs is allowed.
+ * Every out and x_next row is written once.  Requires flags within the two bits, finite
+ * eps >= 0 and every pointer the flags use non-NULL and 16-byte aligned, else
+ * MOE_ERR_INVALID_ARGUMENT.  With eps = 0 an all-zero row gives Inf/NaN (not checked).
+ * flags = 0 gives results bit-identical to moe_combine. */
+#define MOE_COMBINE_EXPERT_NORM 1u
+#define MOE_COMBINE_RESIDUAL_NORM 2u
+moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *slot_row_dev,
+                            const float *topk_w_dev, int32_t T, int32_t k, int32_t H,
+                            uint32_t flags, float eps, const float *resid_dev, float alpha,
+                            float beta, const float *gain_dev, float *out_dev,
+                            uint16_t *x_next_dev, void *stream);
 
 /* The whole layer in one call: route, group, expert FFN and combine, with the same arguments,
  * outputs and meaning as the four calls above (one token: out[t] = sum over the token's k

@@ -131,6 +131,23 @@ def make_zipf_bias(E, s=1.1, seed=0, device="cpu"):
     return (-s * torch.log(rank)).to(torch.float32).to(device)
 
 
+def make_combine_inputs(T, k, H, seed=0, device="cpu", y_dtype=torch.float16):
+    """Inputs of the combine variants.  y [T*k][H]: N(0,1) rows, each scaled by exp(N(0,1)) so
+    the expert rows differ in magnitude (as expert outputs do); slot_row: a seeded permutation
+    of the T*k rows (any grouping is a permutation); topk_w [T][k]: positive, each row summing to
+    one; resid [T][H]: N(0, 9); gain [H]: uniform in [0.5, 1.5]."""
+    d = torch.device(device)
+    g = _gen(d, seed, 20)
+    y = torch.randn((T * k, H), generator=g, device=d, dtype=torch.float32)
+    y *= torch.exp(torch.randn((T * k, 1), generator=g, device=d, dtype=torch.float32))
+    slot_row = torch.randperm(T * k, generator=g, device=d).to(torch.int32)
+    w = torch.rand((T, k), generator=g, device=d, dtype=torch.float32) + 0.05
+    w /= w.sum(dim=1, keepdim=True)
+    resid = torch.randn((T, H), generator=g, device=d, dtype=torch.float32) * 3.0
+    gain = torch.rand((H,), generator=g, device=d, dtype=torch.float32) + 0.5
+    return dict(y=y.to(y_dtype), slot_row=slot_row, topk_w=w, resid=resid, gain=gain)
+
+
 def make_layer(spec, seed=0, device="cpu", T=None, experts=None):
     """All inputs of one layer call for a spec (a SPECS key or a dict with the same fields)."""
     sp = dict(SPECS[spec]) if isinstance(spec, str) else dict(spec)

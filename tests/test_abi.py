@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     for code in (OK, INVALID, SHAPE, WS, -4, -5, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
 
@@ -125,6 +125,29 @@ def test_combine_rejects_bad_arguments():
     assert c(A, 0, A, A + 4, 4, 2, 256, A, None) == INVALID
     assert c(A, 0, A, A, 0, 2, 256, A, None) == INVALID
     assert c(A, 0, A, A, 4, 2, 200, A, None) == SHAPE
+
+
+def _cn(flags=0, eps=1e-6, resid=A, gain=A, out=A, xn=A, y=A, yd=1, H=256, T=4, k=2):
+    return moe.lib().moe_combine_norm(y, yd, A, A, T, k, H, flags, eps, resid, 1.0, 1.0, gain,
+                                      out, xn, None)
+
+
+def test_combine_norm_rejects_bad_arguments():
+    assert _cn(flags=4) == INVALID
+    assert _cn(flags=1, eps=-1.0) == INVALID
+    assert _cn(flags=1, eps=float("inf")) == INVALID
+    assert _cn(flags=1, eps=float("nan")) == INVALID
+    assert _cn(flags=3, resid=None) == INVALID
+    assert _cn(flags=2, gain=None) == INVALID
+    assert _cn(flags=2, xn=None) == INVALID
+    assert _cn(flags=2, xn=A + 8) == INVALID
+    assert _cn(flags=2, resid=A + 4) == INVALID
+    assert _cn(out=A + 4) == INVALID
+    assert _cn(y=None) == INVALID
+    assert _cn(yd=2) == INVALID
+    assert _cn(T=0) == INVALID
+    assert _cn(H=200) == SHAPE
+    assert _cn(H=65536 + 128) == SHAPE
 
 
 def test_python_binding_validates_before_calling():
