@@ -181,6 +181,7 @@ def main():
             traffic = measured_traffic("traffic_layer_small_decode1.txt")
     else:
         kernel, kbytes = "expert FFN call (few-row kernels + grouped GEMM)", ffn_bytes
+        traffic = measured_traffic("traffic_ffn_%s.txt" % wl)
     if big:
         achieved = flops / (ffn_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_F16_PEAK_TFS,
@@ -200,7 +201,9 @@ def main():
                        variant="expert_norm+residual_norm" if norm else "plain",
                        us=round(comb_ms * 1e3, 2), algorithmic_bytes=int(cb),
                        achieved_gbs=round(cb / (comb_ms * 1e-3) / 1e9, 1),
-                       frac=round(cb / (comb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+                       frac=round(cb / (comb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       traffic=measured_traffic("traffic_%s_%s.txt" % (
+                           "combine_norm" if norm else "combine", wl)))
 
     cpu = None
     if args.cpu_seconds > 0:

@@ -9,12 +9,13 @@
 //     residual and next pre-norm in one kernel).
 // RMS norm of a row v: v / sqrt(mean(v^2) + eps).
 //
-// One block of 1024 threads per token; thread i owns the 4-feature groups i, i + 1024, ...
-// (G groups, features [4q, 4q + 4) of group q), so the block reads every row it needs once,
-// coalesced.  Expert rows are loaded KC at a time into registers: their sums of squares are
-// reduced over the block in one round (wavefront butterfly, then 16 wavefront totals through
-// LDS, in a fixed order), and the same registers are then scaled into the fp32 accumulator, so
-// y is read exactly once.  The epilogue needs two more block reductions (f, then the new
+// One block of 512 threads per token (1024 for hidden sizes above 32768, where registers
+// spill); thread i owns the 4-feature groups i, i + NT, ... (G groups, features [4q, 4q + 4)
+// of group q), so the block reads every row it needs once, coalesced.  Expert rows are loaded
+// KC at a time into registers: their sums of squares are reduced over the block in one round
+// (wavefront butterfly, then the wavefront totals through LDS, in a fixed order), and the same
+// registers are then scaled into the fp32 accumulator, so y is read exactly once.  512-thread
+// blocks keep three tokens resident per compute unit at hidden 7168.  The epilogue needs two more block reductions (f, then the new
 // residual) and writes the residual (fp32) and the next input (bf16, round to nearest even)
 // once each.
 #include "common.h"
@@ -23,8 +24,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kCnThreads = 1024;
-constexpr int kCnWaves = kCnThreads / 64;
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 
@@ -58,23 +57,36 @@ __device__ inline f32x4 load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4*)
 __device__ inline f32x4 to_f32(f16x4 v) { return __builtin_convertvector(v, f32x4); }
 __device__ inline f32x4 to_f32(f32x4 v) { return v; }
 
+// sum of squares of four values added to s (f16 pairs through the f32-accumulating dot)
+__device__ inline float add_squares(f16x4 v, float s) {
+  const f16x2 lo = {v.x, v.y}, hi = {v.z, v.w};
+  s = __builtin_amdgcn_fdot2(lo, lo, s, false);
+  return __builtin_amdgcn_fdot2(hi, hi, s, false);
+}
+__device__ inline float add_squares(f32x4 v, float s) {
+  s = fmaf(v.x, v.x, s);
+  s = fmaf(v.y, v.y, s);
+  s = fmaf(v.z, v.z, s);
+  return fmaf(v.w, v.w, s);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-// Sums v[0..N) over the block; every thread gets the totals.  Each wavefront reduces its own
-// values (xor butterfly), lane 0 writes them to red; after the barrier lane l reads wavefront
-// (l % 16)'s value and a 16-lane butterfly adds the 16 wavefront totals.  Every lane ends with
-// the same bits (xor butterflies add the same pairs on both sides).  red is [2][kCnWaves][N]
-// floats, used alternately (phase toggles): a wavefront can only write a buffer again after
-// passing the next reduction's barrier, which every reader of this one reaches only after
-// reading.
-template <int N>
+// Sums v[0..N) over the block of NW wavefronts; every thread gets the totals.  Each wavefront
+// reduces its own values (xor butterfly), lane 0 writes them to red; after the barrier lane l
+// reads wavefront (l % NW)'s value and an NW-lane butterfly adds the wavefront totals.  Every
+// lane ends with the same bits (xor butterflies add the same pairs on both sides).  red is
+// [2][NW][N] floats, used alternately (phase toggles): a wavefront can only write a buffer
+// again after passing the next reduction's barrier, which every reader of this one reaches
+// only after reading.
+template <int N, int NW>
 __device__ inline void block_sum(float (&v)[N], float* red, int& phase) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* buf = red + phase * (kCnWaves * N);
+  float* buf = red + phase * (NW * N);
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
   if (lane == 0) {
@@ -84,9 +96,9 @@ __device__ inline void block_sum(float (&v)[N], float* red, int& phase) {
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    float s = buf[(lane & (kCnWaves - 1)) * N + i];
+    float s = buf[(lane & (NW - 1)) * N + i];
 #pragma unroll
-    for (int m = 1; m < kCnWaves; m <<= 1) s += __shfl_xor(s, m);
+    for (int m = 1; m < NW; m <<= 1) s += __shfl_xor(s, m);
     v[i] = s;
   }
   phase ^= 1;
@@ -104,12 +116,13 @@ constexpr int combine_norm_rows(bool f16, int G) {
 
 }  // namespace
 
-// G: 4-feature groups per thread (H <= 4096 G).
-template <bool Y_F16, int G>
-__global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArgs a) {
+// NT threads per block (one token), G 4-feature groups per thread: H <= 4 NT G.
+template <bool Y_F16, int G, int NT>
+__global__ __launch_bounds__(NT) void combine_norm_kernel(CombineNormArgs a) {
+  constexpr int NW = NT / 64;
   typedef typename RowVec<Y_F16>::type vec_t;
   constexpr int KC = combine_norm_rows(Y_F16, G);
-  __shared__ float red[2 * kCnWaves * KC];
+  __shared__ float red[2 * NW * KC];
   const int t = blockIdx.x;
   const int H = a.H, k = a.k;
   const float inv_h = 1.0f / (float)H;
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArg
   uint32_t qi[G];  // group index (clamped)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int q = g * kCnThreads + threadIdx.x;
+    const int q = g * NT + threadIdx.x;
     valid[g] = q < nq;
     qi[g] = (uint32_t)(valid[g] ? q : nq - 1);
   }
@@ -157,15 +170,9 @@ __global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArg
       for (int i = 0; i < KC; ++i) {
         ss[i] = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const f32x4 f = to_f32(v[i][g]);
-          ss[i] = fmaf(f.x, f.x, ss[i]);
-          ss[i] = fmaf(f.y, f.y, ss[i]);
-          ss[i] = fmaf(f.z, f.z, ss[i]);
-          ss[i] = fmaf(f.w, f.w, ss[i]);
-        }
+        for (int g = 0; g < G; ++g) ss[i] = add_squares(v[i][g], ss[i]);
       }
-      block_sum(ss, red, phase);
+      block_sum<KC, NW>(ss, red, phase);
 #pragma unroll
       for (int i = 0; i < KC; ++i) c[i] *= rms_factor(ss[i], inv_h, a.eps);
     }
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArg
       pgain[g] = load_vec(gain, qi[g] * 16u, (f32x4*)nullptr);
     }
   }
-  block_sum(sf, red, phase);
+  block_sum<1, NW>(sf, red, phase);
   const float bs = a.beta * rms_factor(sf[0], inv_h, a.eps);
   float so[1] = {0.f};
 #pragma unroll
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArg
     so[0] = fmaf(acc[g].w, acc[g].w, so[0]);
     if (valid[g]) out[qi[g]] = acc[g];
   }
-  block_sum(so, red, phase);
+  block_sum<1, NW>(so, red, phase);
   const float r = rms_factor(so[0], inv_h, a.eps);
   bf16x4_t* xn = reinterpret_cast<bf16x4_t*>(a.x_next) + (size_t)t * nq;
 #pragma unroll
@@ -244,23 +251,24 @@ __global__ __launch_bounds__(kCnThreads) void combine_norm_kernel(CombineNormArg
   }
 }
 
-int combine_norm_groups(int H) {
-  int g = 1;
-  while (g * kCnThreads * 4 < H) g <<= 1;
-  return g;
-}
-
+// 512 threads per token up to H = 32768 (G = 1..16 groups per thread), 1024 above.
 hipError_t launch_combine_norm(const CombineNormArgs& a, int y_f16, hipStream_t s) {
-  const int G = combine_norm_groups(a.H);
-  const dim3 grid((unsigned)a.T), block(kCnThreads);
-#define MOE_CN(F16_, G_) combine_norm_kernel<F16_, G_><<<grid, block, 0, s>>>(a)
-#define MOE_CN_G(F16_)            \
-  switch (G) {                    \
-    case 1: MOE_CN(F16_, 1); break; \
-    case 2: MOE_CN(F16_, 2); break; \
-    case 4: MOE_CN(F16_, 4); break; \
-    case 8: MOE_CN(F16_, 8); break; \
-    default: MOE_CN(F16_, 16); break; \
+  int G = 1;
+  while (G * 512 * 4 < a.H && G < 16) G <<= 1;
+  const bool wide = a.H > 512 * 4 * 16;
+  const dim3 grid((unsigned)a.T);
+#define MOE_CN(F16_, G_, NT_) combine_norm_kernel<F16_, G_, NT_><<<grid, dim3(NT_), 0, s>>>(a)
+#define MOE_CN_G(F16_)                 \
+  if (wide) {                          \
+    MOE_CN(F16_, 16, 1024);            \
+  } else {                             \
+    switch (G) {                       \
+      case 1: MOE_CN(F16_, 1, 512); break; \
+      case 2: MOE_CN(F16_, 2, 512); break; \
+      case 4: MOE_CN(F16_, 4, 512); break; \
+      case 8: MOE_CN(F16_, 8, 512); break; \
+      default: MOE_CN(F16_, 16, 512); break; \
+    }                                  \
   }
   if (y_f16) {
     MOE_CN_G(true)

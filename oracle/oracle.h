@@ -10,6 +10,9 @@
  *   router logits  ->  top-k of E experts  ->  softmax over the selected k  ->  grouping of
  *   (token, slot) rows by expert  ->  per row: gate/up projections, SwiGLU, down projection
  *   ->  routing-weighted sum of the k expert outputs of each token.
+ * Combine variants (oracle_combine_norm): each expert output RMS-normalised before the weighted
+ * sum, and the epilogue after it (the MoE output's own RMS factor, the scaled residual
+ * alpha * x + beta * s * f, an RMS norm with a gain for the next layer's input).
  * Sources (the web pages this layer comes from):
  *   - "Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU", Background / "The model":
  *     every token is routed to 8 of 256 experts; "NVFP4 experts": 4-bit expert weights with one
@@ -19,6 +22,10 @@
  *     adds the expert outputs in a weighted sum.
  *   - "Mixture of Experts" topic page, Transformer Engine summary: grouped expert GEMMs with
  *     SwiGLU and routing-weight scaling.
+ *   - Muse Spark page, section 8: each expert's output is normalised before the weighted sum;
+ *     section 3, "What makes this possible is where Muse Spark normalizes": the residual stream
+ *     and the RMS norm (Zhang and Sennrich) that feeds the next layer; "A 501B sparse model gets
+ *     day-one serving support": post-norm, scaled residual and next pre-norm in one kernel.
  *
  * Precision.  Sums, SwiGLU and the combine run in double.  Router logits are summed in double
  * and rounded once to float: the top-k decision is taken on those float logits, in the same
