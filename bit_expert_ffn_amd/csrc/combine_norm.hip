@@ -15,9 +15,9 @@
 // KC at a time into registers: their sums of squares are reduced over the block in one round
 // (wavefront butterfly, then the wavefront totals through LDS, in a fixed order), and the same
 // registers are then scaled into the fp32 accumulator, so y is read exactly once.  512-thread
-// blocks keep three tokens resident per compute unit at hidden 7168.  The epilogue needs two more block reductions (f, then the new
-// residual) and writes the residual (fp32) and the next input (bf16, round to nearest even)
-// once each.
+// blocks keep three tokens resident per compute unit at hidden 7168.  The epilogue needs two
+// more block reductions (f, then the new residual) and writes the residual (fp32) and the next
+// input (bf16, round to nearest even) once each.
 #include "common.h"
 
 namespace moe {

@@ -98,14 +98,38 @@ __device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok) {
   return ok;
 }
 
+// Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
+
+// Selection key of a logit: larger key = larger logit, equal logits -> the lower expert id.  -0
+// counts as +0 and NaN as -inf.  0 is below every key (an empty candidate).
+__device__ inline uint64_t sel_key(float v, int id) {
+  v = v == v ? v + 0.0f : -__builtin_inff();
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+}
+__device__ inline float sel_value(uint64_t key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ inline int sel_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+// Orders the LDS accesses of one wavefront (its lanes read what other lanes just wrote).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 template <int TT, bool VEC>
 __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];  // x rows, later h halves
   __shared__ float red[32][TT][kLsEG];
-  __shared__ __attribute__((aligned(16))) float lv[TT][kMaxExperts];
-  __shared__ float2 cand[TT][4 * kLsMaxSlots];
-  __shared__ int sel_e[kLsMaxSlots];
-  __shared__ float sel_l[kLsMaxSlots];
+  __shared__ uint64_t cand[TT][4 * kLsMaxSlots];
+  __shared__ uint64_t wkey[4][64];                    // per wavefront: its 64 selection keys
+  __shared__ uint64_t wsel[4][TT][kLsMaxSlots];      // per wavefront: the selected slots
   __shared__ int slot_e[kLsMaxSlots], slot_cnt[kLsMaxSlots], slot_first[kLsMaxSlots];
   __shared__ int slot_pos[kLsMaxSlots];
   __shared__ float slot_w[kLsMaxSlots];
@@ -185,192 +209,304 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   for (int i = tid; i < T * H / 8; i += 256)
     reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(a.x)[i];
 
+  // ---- gate/up plan, set up while barrier A completes.  Item = (expert, 16-feature tile) per
+  // wavefront.  With one token the items follow the token's slots (largest logit first), so
+  // that the first weights can be requested as soon as the ranks are known; with two tokens
+  // they follow the active list. ----
+  const int nch = H / kChunk;  // chunks along the hidden dimension
+  const int ntile = I / 16;
+  const int W = G * 4, gw = blockIdx.x * 4 + wv;
+  const int nspi = (nch + kLsSetC - 1) / kLsSetC;  // load sets per item
+  const size_t mq = (size_t)I * H / 2, ms = (size_t)I * H / 16;
+  const int* c_e = TT == 1 ? slot_e : act_e;      // item's expert
+  const int* c_off = TT == 1 ? slot_pos : act_off;  // item's first row in the grouped order
+  int na = 0, n_items = 0, nsets = 0;
+  auto plan = [&](int nact) {
+    na = nact;
+    n_items = na * ntile;
+    const int my_items = gw < n_items ? (n_items - 1 - gw) / W + 1 : 0;
+    nsets = my_items * nspi;
+  };
+  // A cursor walks the wavefront's load sets: set j of item it = gw + m W (item-list index ai,
+  // 16-feature tile rt).  Past the last set it stays there (loads re-read it, unused).
+  struct Cur {
+    int j, it, ai, rt;
+  };
+  auto cur_item = [&](Cur& c, int it) {
+    c.j = 0;
+    c.it = it;
+    c.ai = it / ntile;
+    c.rt = it - c.ai * ntile;
+  };
+  auto cur_next = [&](Cur& c) {
+    if (c.j + 1 < nspi) {
+      ++c.j;
+    } else if (c.it + W < n_items) {
+      cur_item(c, c.it + W);
+    }
+  };
+  uint4 qgA[kLsSetC], quA[kLsSetC], qgB[kLsSetC], quB[kLsSetC];
+  uint32_t sgA[kLsSetC], suA[kLsSetC], sgB[kLsSetC], suB[kLsSetC];
+  auto load_set = [&](uint4* qg, uint4* qu, uint32_t* sg, uint32_t* su, const Cur& c, int e) {
+    const int cs = c.j * kLsSetC;
+    const size_t tq = (size_t)e * mq + ((size_t)c.rt * nch) * 1024 + lane * 16;
+    const size_t ts_ = (size_t)e * ms + ((size_t)c.rt * nch) * 128 + lane * 2;
+#pragma unroll
+    for (int u = 0; u < kLsSetC; ++u) {
+      const int ch = min(cs + u, nch - 1);
+      qg[u] = *reinterpret_cast<const uint4*>(a.gq + tq + (size_t)ch * 1024);
+      qu[u] = *reinterpret_cast<const uint4*>(a.uq + tq + (size_t)ch * 1024);
+      sg[u] = load_u16(a.gs + ts_ + (size_t)ch * 128);
+      su[u] = load_u16(a.us + ts_ + (size_t)ch * 128);
+    }
+  };
+  Cur lc, uc;
+  if constexpr (TT == 1) {
+    plan(k);  // one token: k distinct experts
+    cur_item(lc, gw);
+    uc = lc;
+  }
+
   // ---- B: logits, top-k, softmax, grouping (every block) ----
   if (!ls_wait(a.sync, kLsFlagA, &s_flag)) return;
-  {
-    const int e = tid;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t >= T) break;
-      if (e < E) {
-        float v[kLsNS];
-#pragma unroll
-        for (int sl = 0; sl < kLsNS; ++sl)
-          v[sl] = a.partial[((size_t)sl * T + t) * E + e];
-        float s = 0.f;
-#pragma unroll
-        for (int sl = 0; sl < kLsNS; ++sl) s += v[sl];
-        if (a.bias) s += a.bias[e];
-        if (blockIdx.x == 0 && a.logits) a.logits[(size_t)t * E + e] = s;
-        lv[t][e] = s;
-      } else {
-        lv[t][e] = -__builtin_inff();  // never larger than a real logit
-      }
-    }
-  }
-  __syncthreads();
-  // top-k in two levels.  An expert's rank is the number of experts with a larger logit plus
-  // those with an equal logit and a lower id.  Each wavefront first ranks its 64 experts among
-  // themselves; those of local rank < k are the candidates (the overall top k are among them),
-  // and the 4k candidates are then ranked among each other.
+  // logits of expert e = tid (slices added in order), kept in registers
+  float lg[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    if (t >= T) break;
-    const float le = lv[t][tid];
-    const f32x4* lp = reinterpret_cast<const f32x4*>(&lv[t][wv * 64]);
-    int rl = 0;
-#pragma unroll 4
-    for (int j = 0; j < 16; ++j) {
-      const f32x4 v = lp[j];
+    lg[t] = -__builtin_inff();
+    if (tid < E) {
+      float v[kLsNS];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        rl += (v[c] > le) | ((v[c] == le) & (wv * 64 + 4 * j + c < tid));
+      for (int sl = 0; sl < kLsNS; ++sl) v[sl] = a.partial[((size_t)sl * T + t) * E + tid];
+      float sum = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < kLsNS; ++sl) sum += v[sl];
+      if (a.bias) sum += a.bias[tid];
+      if (blockIdx.x == 0 && a.logits) a.logits[(size_t)t * E + tid] = sum;
+      lg[t] = sum;
     }
-    // candidates as (logit, id) pairs; missing ones (fewer than k experts in the wavefront)
-    // are (-inf, INT_MAX), which never count as larger
-    if (tid < E && rl < k) cand[t][wv * k + rl] = make_float2(le, __int_as_float(tid));
-    if (lane < k && wv * 64 + lane >= E)
-      cand[t][wv * k + lane] = make_float2(-__builtin_inff(), __int_as_float(0x7fffffff));
   }
-  __syncthreads();
+  // top-k in two levels, by rank: an expert's rank is the number of experts with a larger
+  // selection key (a larger logit, or an equal logit and a lower id).  Each lane first ranks
+  // its expert among the 64 of its wavefront; those of rank < k are the candidates (the overall
+  // top k are among them).  Then every wavefront (redundantly, so that no second barrier is
+  // needed) ranks the 4k candidates among each other.  All comparisons are independent, so the
+  // wavefront issues them back to back.
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    if (t >= T) break;
+    const uint64_t key = tid < E ? sel_key(lg[t], tid) : 0;
+    wkey[wv][lane] = key;
+    if (lane < k) cand[t][wv * k + lane] = 0;
+    wave_lds_sync();
+    int rank = 0;
+    const uint4* kp = reinterpret_cast<const uint4*>(wkey[wv]);
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const uint4 v = kp[j];
+      rank += (((uint64_t)v.y << 32) | v.x) > key;
+      rank += (((uint64_t)v.w << 32) | v.z) > key;
+    }
+    if (key != 0 && rank < k) cand[t][wv * k + rank] = key;
+    wave_lds_sync();
+  }
+  lds_barrier();
+  // candidate keys (two per lane) and their ranks among the candidates
+  uint64_t cc0[TT], cc1[TT];
+  int rr0[TT], rr1[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
     const int nc = 4 * k;
-    if (tid < nc) {
-      const float2 me = cand[t][tid];
-      const float le = me.x;
-      const int e = __float_as_int(me.y);
-      int r = 0;
-      for (int c0 = 0; c0 < nc; c0 += 8) {
-        float2 v[8];
+    cc0[t] = lane < nc ? cand[t][lane] : 0;
+    cc1[t] = lane + 64 < nc ? cand[t][lane + 64] : 0;
+    int r0 = 0, r1 = 0;
+    const uint4* cp = reinterpret_cast<const uint4*>(cand[t]);
+    for (int j = 0; j < nc / 2; ++j) {  // nc is even
+      const uint4 v = cp[j];
+      const uint64_t v0 = ((uint64_t)v.y << 32) | v.x, v1 = ((uint64_t)v.w << 32) | v.z;
+      r0 += (v0 > cc0[t]) + (v1 > cc0[t]);
+      r1 += (v0 > cc1[t]) + (v1 > cc1[t]);
+    }
+    rr0[t] = r0;
+    rr1[t] = r1;
+  }
+  if constexpr (TT == 1) {
+    // the first two gate/up load sets are requested now: the expert of slot r is the candidate
+    // of rank r
+    auto slot_expert = [&](int r) {
+      const uint64_t m0 = __ballot(cc0[0] != 0 && rr0[0] == r);
+      const uint64_t m1 = __ballot(cc1[0] != 0 && rr1[0] == r);
+      const int i0 = __builtin_amdgcn_readlane(sel_id(cc0[0]) , m0 ? (int)__builtin_ctzll(m0) : 0);
+      const int i1 = __builtin_amdgcn_readlane(sel_id(cc1[0]), m1 ? (int)__builtin_ctzll(m1) : 0);
+      return m0 ? i0 : (m1 ? i1 : 0);
+    };
+    if (nsets > 0) {
+      load_set(qgA, quA, sgA, suA, lc, slot_expert(lc.ai));
+      cur_next(lc);
+      load_set(qgB, quB, sgB, suB, lc, slot_expert(lc.ai));
+      cur_next(lc);
+    }
+  }
+  // each token's slots into lanes (lane r < k: slot r), through this wavefront's LDS
+  uint64_t sk[TT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = cand[t][min(c0 + u, nc - 1)];
+  for (int t = 0; t < TT; ++t) {
+    if (lane < k) wsel[wv][t][lane] = 0;
+    wave_lds_sync();
+    if (cc0[t] != 0 && rr0[t] < k) wsel[wv][t][rr0[t]] = cc0[t];
+    if (cc1[t] != 0 && rr1[t] < k) wsel[wv][t][rr1[t]] = cc1[t];
+    wave_lds_sync();
+    sk[t] = lane < k ? wsel[wv][t][lane] : 0;
+  }
+  // softmax over each token's k selected logits (lanes r < k)
+  float sw[TT];
+  int se[TT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (c0 + u < nc)
-            r += (v[u].x > le) | ((v[u].x == le) & (__float_as_int(v[u].y) < e));
-      }
-      if (r < k && e != 0x7fffffff) {
-        sel_e[t * k + r] = e;
-        sel_l[t * k + r] = le;
+  for (int t = 0; t < TT; ++t) {
+    const float l = sel_value(sk[t]);
+    const float l0 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(l)));  // slot 0
+    const float ex = lane < k ? expf(l - l0) : 0.f;
+    sw[t] = ex / __ockl_wfred_add_f32(ex);
+    se[t] = lane < k ? sel_id(sk[t]) : 0;
+  }
+  if constexpr (TT == 1) {
+    // one token: its k experts are distinct, each with one row; the grouped order (and the
+    // active order: count descending, id ascending) is expert id ascending
+    int pos = 0;  // lane r < k: position of slot r in the grouped order
+    const uint4* sp = reinterpret_cast<const uint4*>(wsel[wv][0]);
+    for (int j = 0; j < (k + 1) / 2; ++j) {
+      const uint4 v = sp[j];
+      pos += (2 * j < k) & (sel_id(((uint64_t)v.y << 32) | v.x) < se[0]);
+      pos += (2 * j + 1 < k) & (sel_id(((uint64_t)v.w << 32) | v.z) < se[0]);
+    }
+    if (wv == 0 && lane < k) {
+      slot_e[lane] = se[0];
+      slot_pos[lane] = pos;
+      act_e[pos] = se[0];
+      act_cnt[pos] = 1;
+      act_off[pos] = pos;
+      srow_tok[pos] = 0;
+      srow_w[pos] = sw[0];
+      if (blockIdx.x == 0) {
+        a.topk_id[lane] = se[0];
+        a.topk_w[lane] = sw[0];
+        a.sorted_slot[pos] = lane;
+        a.slot_row[lane] = pos;
       }
     }
-  }
-  __syncthreads();
-  if (tid < nq) {
-    const int t = tid / k;
-    const float m = sel_l[t * k];
-    float den = 0.f;
-    for (int i = 0; i < k; ++i) den += expf(sel_l[t * k + i] - m);
-    const float w = expf(sel_l[tid] - m) / den;
-    slot_e[tid] = sel_e[tid];
-    slot_w[tid] = w;
     if (blockIdx.x == 0) {
-      a.topk_id[tid] = sel_e[tid];
-      a.topk_w[tid] = w;
-    }
-  }
-  __syncthreads();
-  if (tid < nq) {
-    // stable counting sort of the slots by expert: position = slots of smaller experts + earlier
-    // slots of the same expert
-    const int e = slot_e[tid];
-    int cnt = 0, r = 0, off = 0;
-    for (int q = 0; q < nq; ++q) {
-      const int eq = slot_e[q];
-      cnt += eq == e;
-      r += (eq == e) & (q < tid);
-      off += eq < e;
-    }
-    const int pos = off + r;
-    slot_cnt[tid] = cnt;
-    slot_first[tid] = r == 0;
-    slot_pos[tid] = pos;
-    srow_tok[pos] = tid / k;
-    srow_w[pos] = slot_w[tid];
-    if (blockIdx.x == 0) {
-      a.sorted_slot[pos] = tid;
-      a.slot_row[tid] = pos;
-    }
-  }
-  __syncthreads();
-  if (tid < nq && slot_first[tid]) {
-    // active order: count descending, then expert id ascending
-    const int e = slot_e[tid], cnt = slot_cnt[tid];
-    int ar = 0;
-    for (int q = 0; q < nq; ++q) {
-      if (slot_first[q]) {
-        const int c2 = slot_cnt[q], e2 = slot_e[q];
-        ar += (c2 > cnt) | ((c2 == cnt) & (e2 < e));
+      for (int e = tid; e < E; e += 256) {
+        int c = 0, o = 0, act = -1;
+        for (int r = 0; r < k; ++r) {
+          const int er = __builtin_amdgcn_readlane(se[0], r);
+          c += er == e;
+          o += er < e;
+          if (__builtin_amdgcn_readlane(pos, r) == e) act = er;
+        }
+        a.count[e] = c;
+        a.offset[e] = o;
+        a.active[e] = act;
+      }
+      if (tid == 0) {
+        a.offset[E] = k;
+        *a.n_active = k;
       }
     }
-    act_e[ar] = e;
-    act_cnt[ar] = cnt;
-    act_off[ar] = slot_pos[tid];
-  }
-  if (tid == 0) {
-    int na = 0;
-    for (int q = 0; q < nq; ++q) na += slot_first[q];
-    s_nact = na;
-  }
-  __syncthreads();
-  const int na = s_nact;
-  if (blockIdx.x == 0) {
-    for (int e = tid; e < E; e += 256) {
-      int c = 0, o = 0;
+    lds_barrier();
+  } else {
+    if (wv == 0 && lane < k) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (t < T) {
+          slot_e[t * k + lane] = se[t];
+          slot_w[t * k + lane] = sw[t];
+          if (blockIdx.x == 0) {
+            a.topk_id[t * k + lane] = se[t];
+            a.topk_w[t * k + lane] = sw[t];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < nq) {
+      // stable counting sort of the slots by expert: position = slots of smaller experts + earlier
+      // slots of the same expert
+      const int e = slot_e[tid];
+      int cnt = 0, r = 0, off = 0;
       for (int q = 0; q < nq; ++q) {
-        c += slot_e[q] == e;
-        o += slot_e[q] < e;
+        const int eq = slot_e[q];
+        cnt += eq == e;
+        r += (eq == e) & (q < tid);
+        off += eq < e;
       }
-      a.count[e] = c;
-      a.offset[e] = o;
-      a.active[e] = e < na ? act_e[e] : -1;
+      const int pos = off + r;
+      slot_cnt[tid] = cnt;
+      slot_first[tid] = r == 0;
+      slot_pos[tid] = pos;
+      srow_tok[pos] = tid / k;
+      srow_w[pos] = slot_w[tid];
+      if (blockIdx.x == 0) {
+        a.sorted_slot[pos] = tid;
+        a.slot_row[tid] = pos;
+      }
+    }
+    __syncthreads();
+    if (tid < nq && slot_first[tid]) {
+      // active order: count descending, then expert id ascending
+      const int e = slot_e[tid], cnt = slot_cnt[tid];
+      int ar = 0;
+      for (int q = 0; q < nq; ++q) {
+        if (slot_first[q]) {
+          const int c2 = slot_cnt[q], e2 = slot_e[q];
+          ar += (c2 > cnt) | ((c2 == cnt) & (e2 < e));
+        }
+      }
+      act_e[ar] = e;
+      act_cnt[ar] = cnt;
+      act_off[ar] = slot_pos[tid];
     }
     if (tid == 0) {
-      a.offset[E] = nq;
-      *a.n_active = na;
+      int nact = 0;
+      for (int q = 0; q < nq; ++q) nact += slot_first[q];
+      s_nact = nact;
+    }
+    __syncthreads();
+    plan(s_nact);
+    if (blockIdx.x == 0) {
+      for (int e = tid; e < E; e += 256) {
+        int c = 0, o = 0;
+        for (int q = 0; q < nq; ++q) {
+          c += slot_e[q] == e;
+          o += slot_e[q] < e;
+        }
+        a.count[e] = c;
+        a.offset[e] = o;
+        a.active[e] = e < na ? act_e[e] : -1;
+      }
+      if (tid == 0) {
+        a.offset[E] = nq;
+        *a.n_active = na;
+      }
+    }
+    cur_item(lc, gw);
+    uc = lc;
+    if (nsets > 0) {
+      load_set(qgA, quA, sgA, suA, lc, act_e[lc.ai]);
+      cur_next(lc);
+      load_set(qgB, quB, sgB, suB, lc, act_e[lc.ai]);
+      cur_next(lc);
     }
   }
 
-  // ---- C: gate/up + SwiGLU; item = (active expert, 16-feature tile) per wavefront ----
+  // ---- C: gate/up + SwiGLU; rows of h (f16) go out with device-scope stores ----
   {
-    const int nch = H / kChunk;  // chunks along the hidden dimension
-    const int ntile = I / 16;
-    const int n_items = na * ntile;
-    const int W = G * 4, gw = blockIdx.x * 4 + wv;
-    const int nspi = (nch + kLsSetC - 1) / kLsSetC;  // load sets per item
-    const int my_items = gw < n_items ? (n_items - 1 - gw) / W + 1 : 0;
-    const int nsets = my_items * nspi;
-    const size_t mq = (size_t)I * H / 2, ms = (size_t)I * H / 16;
-    uint4 qgA[kLsSetC], quA[kLsSetC], qgB[kLsSetC], quB[kLsSetC];
-    uint32_t sgA[kLsSetC], suA[kLsSetC], sgB[kLsSetC], suB[kLsSetC];
-    auto load_set = [&](uint4* qg, uint4* qu, uint32_t* sg, uint32_t* su, int s) {
-      s = min(s, nsets - 1);  // past the end: re-read the last set (unused)
-      const int it = gw + (s / nspi) * W;
-      const int ai = it / ntile, rt = it - ai * ntile;
-      const int e = act_e[ai];
-      const int cs = (s % nspi) * kLsSetC;
-      const size_t tq = (size_t)e * mq + ((size_t)rt * nch) * 1024 + lane * 16;
-      const size_t ts_ = (size_t)e * ms + ((size_t)rt * nch) * 128 + lane * 2;
-#pragma unroll
-      for (int u = 0; u < kLsSetC; ++u) {
-        const int c = min(cs + u, nch - 1);
-        qg[u] = *reinterpret_cast<const uint4*>(a.gq + tq + (size_t)c * 1024);
-        qu[u] = *reinterpret_cast<const uint4*>(a.uq + tq + (size_t)c * 1024);
-        sg[u] = load_u16(a.gs + ts_ + (size_t)c * 128);
-        su[u] = load_u16(a.us + ts_ + (size_t)c * 128);
-      }
-    };
     float ag[TT], au[TT];
 #pragma unroll
     for (int r = 0; r < TT; ++r) ag[r] = au[r] = 0.f;
     auto use_set = [&](const uint4* qg, const uint4* qu, const uint32_t* sg, const uint32_t* su,
-                       int s) {
-      const int it = gw + (s / nspi) * W;
-      const int ai = it / ntile, rt = it - ai * ntile;
-      const int rows = act_cnt[ai], off = act_off[ai];
-      const int cs = (s % nspi) * kLsSetC;
+                       const Cur& cu) {
+      const int ai = cu.ai, rt = cu.rt;
+      const int rows = TT == 1 ? 1 : act_cnt[ai], off = c_off[ai];
+      const int cs = cu.j * kLsSetC;
 #pragma unroll
       for (int u = 0; u < kLsSetC; ++u) {
         const int c = cs + u;
@@ -389,8 +525,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
           }
         }
       }
-      if (s % nspi == nspi - 1) {  // the item's last set: SwiGLU and store two features per lane
-        const int e = act_e[ai];
+      if (cu.j == nspi - 1) {  // the item's last set: SwiGLU and store two features per lane
+        const int e = c_e[ai];
         const float tsg = a.ts[e * 3 + 0], tsu = a.ts[e * 3 + 1];
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
@@ -406,13 +542,28 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         }
       }
     };
+
+    // two load sets in flight: set s + 1 is requested before set s is used
     if (nsets > 0) {
-      load_set(qgA, quA, sgA, suA, 0);
-      for (int s = 0; s < nsets; s += 2) {
-        load_set(qgB, quB, sgB, suB, s + 1);
-        use_set(qgA, quA, sgA, suA, s);
-        load_set(qgA, quA, sgA, suA, s + 2);
-        if (s + 1 < nsets) use_set(qgB, quB, sgB, suB, s + 1);
+      use_set(qgA, quA, sgA, suA, uc);
+      cur_next(uc);
+      load_set(qgA, quA, sgA, suA, lc, c_e[lc.ai]);
+      cur_next(lc);
+      if (1 < nsets) {
+        use_set(qgB, quB, sgB, suB, uc);
+        cur_next(uc);
+      }
+      for (int s = 2; s < nsets; s += 2) {
+        load_set(qgB, quB, sgB, suB, lc, c_e[lc.ai]);
+        cur_next(lc);
+        use_set(qgA, quA, sgA, suA, uc);
+        cur_next(uc);
+        load_set(qgA, quA, sgA, suA, lc, c_e[lc.ai]);
+        cur_next(lc);
+        if (s + 1 < nsets) {
+          use_set(qgB, quB, sgB, suB, uc);
+          cur_next(uc);
+        }
       }
     }
   }
@@ -595,3 +746,4 @@ hipError_t launch_layer_small(const LayerSmallArgs& a, hipStream_t s) {
 }
 
 }  // namespace moe
+
