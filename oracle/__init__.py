@@ -49,6 +49,8 @@ def _load():
         _lib.oracle_weight.restype = ctypes.c_double
         _lib.oracle_weight.argtypes = [ctypes.POINTER(_Experts)] + [ctypes.c_int] * 4
         _lib.oracle_threads.restype = ctypes.c_int
+        _lib.oracle_mx_exp.restype = ctypes.c_int
+        _lib.oracle_e4m3_code.restype = ctypes.c_int
     return _lib
 
 
@@ -253,3 +255,88 @@ def layer_tokens(x_bits, w_router, bias, experts, k, tokens):
     _load().oracle_layer_tokens(_p(x_bits), _p(w_router), _p(b), ctypes.byref(s), H, E, k,
                                 _p(tok), n, _p(logits), _p(ids), _p(w), _p(out))
     return dict(logits=logits, topk_id=ids, topk_w=w, out=out)
+
+
+# ------------------------------------------------------------ low precision: fp8 compute (MX)
+def mx_exp(amax, emax):
+    return _load().oracle_mx_exp(ctypes.c_double(amax), int(emax))
+
+
+def e4m3_code(v):
+    return _load().oracle_e4m3_code(ctypes.c_double(v))
+
+
+def mx_scale(byte):
+    return 2.0 ** (int(byte) - 127)
+
+
+def mx8_quant(v):
+    """MXFP8 (e4m3 codes, e8m0 scale per 32 consecutive values) of a float64 array whose last
+    dimension is a multiple of 32: (codes uint8, scales uint8)."""
+    v = _c(v, np.float64)
+    shape = v.shape
+    flat = v.reshape(-1)
+    codes = np.empty(flat.size, np.uint8)
+    scales = np.empty(flat.size // 32, np.uint8)
+    _load().oracle_mx8_quant(_p(flat), flat.size, _p(codes), _p(scales))
+    return codes.reshape(shape), scales.reshape(shape[:-1] + (shape[-1] // 32,))
+
+
+def mx8_dequant(codes, scales):
+    t8 = np.array([e4m3(c) for c in range(256)])
+    v = t8[np.asarray(codes, np.int64)]
+    return v * np.repeat(2.0 ** (np.asarray(scales, np.int64) - 127), 32, axis=-1)
+
+
+class Mx8Experts:
+    """MXFP8 expert weights, logical row-major: *_q [E][N][K] e4m3 codes, *_s [E][N][K/32] e8m0
+    scale bytes; gate/up N = I, K = H; down N = H, K = I."""
+
+    def __init__(self, gate_q, up_q, down_q, gate_s, up_s, down_s):
+        self.gate_q, self.up_q, self.down_q = (_c(a, np.uint8) for a in (gate_q, up_q, down_q))
+        self.gate_s, self.up_s, self.down_s = (_c(a, np.uint8) for a in (gate_s, up_s, down_s))
+        self.E, self.I, self.H = self.gate_q.shape
+
+
+def nvfp4_to_mxfp8(experts):
+    """Requantise every NVFP4 matrix to MXFP8 (tensor scales folded in): Mx8Experts."""
+    s = experts._struct()
+    out = []
+    for m in range(3):
+        N = experts.H if m == 2 else experts.I
+        K = experts.I if m == 2 else experts.H
+        q = np.empty((experts.E, N, K), np.uint8)
+        sc = np.empty((experts.E, N, K // 32), np.uint8)
+        _load().oracle_nvfp4_to_mxfp8(ctypes.byref(s), m, _p(q), _p(sc))
+        out.append((q, sc))
+    return Mx8Experts(out[0][0], out[1][0], out[2][0], out[0][1], out[1][1], out[2][1])
+
+
+def mx8_weights(mx, e, m):
+    """Dequantised MXFP8 matrix m of expert e, float64 [N][K]."""
+    q = (mx.gate_q, mx.up_q, mx.down_q)[m][e]
+    s = (mx.gate_s, mx.up_s, mx.down_s)[m][e]
+    return mx8_dequant(q, s)
+
+
+def expert_rows_mx(x_bits, mx, e, tokens):
+    """Expert e's FFN in the fp8 (MX) variant on the listed token rows: y float64 [n][H]."""
+    x_bits = _c(x_bits, np.uint16)
+    tok = _c(tokens, np.int32)
+    y = np.empty((len(tok), mx.H), np.float64)
+    _load().oracle_expert_rows_mx(_p(x_bits), mx.H, mx.I, int(e), _p(mx.gate_q), _p(mx.gate_s),
+                                  _p(mx.up_q), _p(mx.up_s), _p(mx.down_q), _p(mx.down_s),
+                                  _p(tok), len(tok), _p(y))
+    return y
+
+
+def ffn_mx(x_bits, mx, grouping, k):
+    """y [T*k][H] (float64) of the fp8 variant in grouped row order."""
+    off = grouping["offset"]
+    ss = grouping["sorted_slot"]
+    y = np.empty((len(ss), mx.H), np.float64)
+    for e in range(mx.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            y[a:b] = expert_rows_mx(x_bits, mx, e, ss[a:b] // k)
+    return y

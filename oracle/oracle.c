@@ -260,3 +260,111 @@ void oracle_layer_tokens(const uint16_t *x, const float *w_router, const float *
   }
   free(y);
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * Low-precision variant: fp8 compute, MXFP8 weights and activations (OCP Microscaling Formats
+ * v1.0).  "Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU" runs fp8 compute with NVFP4
+ * expert weights (Figure 1).  The MX format shares one power-of-two scale X = 2^E (an e8m0 byte
+ * E + 127) between 32 consecutive values: E = floor(log2(amax)) - 8 (8 = the largest exponent of
+ * e4m3); each element is rounded to e4m3 to nearest, ties to even, and saturates at 448.  The
+ * NVFP4 weights (e2m1 * e4m3 * fp32 tensor scale, exact in double) are requantised to MXFP8 once;
+ * x and h are quantised to MXFP8 where they enter a product.  Readings: amax == 0 gives E = -127
+ * and zero codes; E is clamped to [-127, 127]; a negative value keeps its sign bit even when its
+ * magnitude rounds to zero. */
+
+int oracle_mx_exp(double amax, int emax) {
+  if (!(amax > 0.0)) return -127;
+  int ex;
+  frexp(amax, &ex);       /* amax = f * 2^ex, f in [0.5, 1): floor(log2(amax)) = ex - 1 */
+  int E = ex - 1 - emax;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+/* nearest integer, ties to even (the default rounding mode) */
+static double rne(double v) { return nearbyint(v); }
+
+int oracle_e4m3_code(double v) {
+  const int sign = v < 0 ? 0x80 : 0;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) return sign | (int)rne(ldexp(a, 9)); /* subnormals, step 2^-9 */
+  int ex;
+  frexp(a, &ex);
+  int e = ex - 1;                             /* 2^e <= a < 2^(e+1), e in [-6, 8] */
+  int m = (int)rne((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8) { m = 0; ++e; }
+  return sign | ((e + 7) << 3) | m;
+}
+
+double oracle_mx_scale(int byte) { return ldexp(1.0, byte - 127); }
+
+/* MXFP8 quantisation of n values (n a multiple of 32): codes[n], scales[n / 32]. */
+void oracle_mx8_quant(const double *v, int n, uint8_t *codes, uint8_t *scales) {
+  for (int b = 0; b < n / 32; ++b) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[32 * b + i]));
+    const int E = oracle_mx_exp(amax, 8);
+    scales[b] = (uint8_t)(E + 127);
+    for (int i = 0; i < 32; ++i)
+      codes[32 * b + i] = amax > 0.0 ? (uint8_t)oracle_e4m3_code(ldexp(v[32 * b + i], -E)) : 0;
+  }
+}
+
+/* NVFP4 matrix m (0 gate, 1 up, 2 down) of every expert -> MXFP8 in the logical row-major
+ * layout: q8 [E][N][K] e4m3 codes, s8 [E][N][K/32] e8m0 scale bytes. */
+void oracle_nvfp4_to_mxfp8(const oracle_experts *w, int m, uint8_t *q8, uint8_t *s8) {
+  const int N = (m == 2) ? w->H : w->I;
+  const int K = (m == 2) ? w->I : w->H;
+#pragma omp parallel for schedule(static)
+  for (int row = 0; row < w->E * N; ++row) {
+    const int e = row / N, n = row % N;
+    double *v = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int kk = 0; kk < K; ++kk) v[kk] = oracle_weight(w, e, m, n, kk);
+    oracle_mx8_quant(v, K, q8 + (size_t)row * K, s8 + (size_t)row * (K / 32));
+    free(v);
+  }
+}
+
+static double mx8_value(const uint8_t *q, const uint8_t *s, int K, size_t row, int kk) {
+  return oracle_e4m3(q[row * K + kk]) * oracle_mx_scale(s[row * (K / 32) + kk / 32]);
+}
+
+/* Expert e's FFN on token rows tok[0..nrows) in the fp8 variant: x rows -> MXFP8; gate/up with
+ * the MXFP8 weights (exact products, sums in double); h = silu(g) * u -> MXFP8; down -> y. */
+void oracle_expert_rows_mx(const uint16_t *x, int H, int I, int e, const uint8_t *gq,
+                           const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                           const uint8_t *dq, const uint8_t *ds, const int32_t *tok, int nrows,
+                           double *y) {
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < nrows; ++r) {
+    const int L = H > I ? H : I;
+    double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hv = (double *)malloc(sizeof(double) * (size_t)I);
+    uint8_t *c8 = (uint8_t *)malloc((size_t)L);
+    uint8_t *s8 = (uint8_t *)malloc((size_t)L / 32);
+    for (int k = 0; k < H; ++k) xv[k] = oracle_bf16(x[(size_t)tok[r] * H + k]);
+    oracle_mx8_quant(xv, H, c8, s8);
+    for (int k = 0; k < H; ++k) xv[k] = oracle_e4m3(c8[k]) * oracle_mx_scale(s8[k / 32]);
+    for (int f = 0; f < I; ++f) {
+      double g = 0.0, u = 0.0;
+      const size_t row = (size_t)e * I + f;
+      for (int k = 0; k < H; ++k) {
+        g += xv[k] * mx8_value(gq, gs, H, row, k);
+        u += xv[k] * mx8_value(uq, us, H, row, k);
+      }
+      hv[f] = g / (1.0 + exp(-g)) * u;
+    }
+    oracle_mx8_quant(hv, I, c8, s8);
+    for (int f = 0; f < I; ++f) hv[f] = oracle_e4m3(c8[f]) * oracle_mx_scale(s8[f / 32]);
+    for (int n = 0; n < H; ++n) {
+      double acc = 0.0;
+      const size_t row = (size_t)e * H + n;
+      for (int f = 0; f < I; ++f) acc += hv[f] * mx8_value(dq, ds, I, row, f);
+      y[(size_t)r * H + n] = acc;
+    }
+    free(xv);
+    free(hv);
+    free(c8);
+    free(s8);
+  }
+}

@@ -87,6 +87,17 @@ void oracle_combine_norm(const double *y, const int32_t *slot_row, const double 
 void oracle_layer_tokens(const uint16_t *x, const float *w_router, const float *bias,
                          const oracle_experts *w, int H, int E, int k, const int32_t *tokens,
                          int ntok, float *logits, int32_t *topk_id, double *topk_w, double *out);
+/* Low-precision variant (fp8 compute, OCP MX): MXFP8 weights requantised from NVFP4, MXFP8
+ * activations and h.  Definitions and readings in oracle.c. */
+int oracle_mx_exp(double amax, int emax);          /* shared exponent E (scale byte E + 127) */
+int oracle_e4m3_code(double v);                    /* nearest e4m3 code, ties to even, saturated */
+double oracle_mx_scale(int byte);                  /* e8m0 byte -> 2^(byte - 127) */
+void oracle_mx8_quant(const double *v, int n, uint8_t *codes, uint8_t *scales);
+void oracle_nvfp4_to_mxfp8(const oracle_experts *w, int m, uint8_t *q8, uint8_t *s8);
+void oracle_expert_rows_mx(const uint16_t *x, int H, int I, int e, const uint8_t *gq,
+                           const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                           const uint8_t *dq, const uint8_t *ds, const int32_t *tok, int nrows,
+                           double *y);
 /* Threads the oracle's parallel loops use (1 without OpenMP). */
 int oracle_threads(void);
 

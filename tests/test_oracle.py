@@ -516,3 +516,113 @@ def test_combine_norm_chain_matches_torch_rms_norm():
     assert np.allclose(got["f"], f.numpy(), rtol=1e-12, atol=1e-14)
     assert np.allclose(got["out"], out.numpy(), rtol=1e-12, atol=1e-14)
     assert np.allclose(got["xn"], xn.numpy(), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- low precision: fp8 (MX) variant
+def test_mx_exp_closed_form():
+    for j in range(-20, 20):
+        assert oracle.mx_exp(2.0 ** j, 8) == j - 8
+        assert oracle.mx_exp(2.0 ** j * 1.999, 8) == j - 8
+        assert oracle.mx_exp(2.0 ** j * 0.999, 8) == j - 9
+    assert oracle.mx_exp(0.0, 8) == -127
+    assert oracle.mx_exp(2.0 ** -200, 8) == -127   # clamped
+    assert oracle.mx_exp(2.0 ** 200, 8) == 127
+
+
+def test_e4m3_code_round_trip_and_torch():
+    """Every finite code (but -0) round-trips; random values round as torch's float8_e4m3fn
+    cast does (to nearest, ties to even) below the saturation point; at or above 448 the code
+    saturates."""
+    for c in range(256):
+        if c in (0x7F, 0xFF, 0x80):
+            continue
+        assert oracle.e4m3_code(oracle.e4m3(c)) == c, c
+    rng = np.random.default_rng(31)
+    v = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.uniform(-4, 2.3, 2000),
+                        [2.0 ** -10, 3 * 2.0 ** -11, 1.0625, 1.1875, 447.9, -0.0009]])
+    v = v[np.abs(v) < 448]
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_code(x) for x in v], np.uint8)
+    zero = (want & 0x7F) == 0          # a negative value rounding to zero: -0 on both sides
+    assert np.array_equal(got[~zero], want[~zero])
+    assert np.all((got[zero] & 0x7F) == 0)
+    # ties to the even mantissa, saturation
+    assert oracle.e4m3_code(1.0625) == 0x38 and oracle.e4m3_code(1.1875) == 0x3A
+    assert oracle.e4m3_code(448.0) == 0x7E and oracle.e4m3_code(1e6) == 0x7E
+    assert oracle.e4m3_code(-500.0) == 0xFE
+
+
+def test_mx8_quant_is_nearest_on_the_scaled_grid():
+    """Brute force over all 254 finite e4m3 codes: each quantised value is a nearest point of the
+    block's scaled grid (scale 2^(floor(log2 amax) - 8)); an all-zero block gives zero codes."""
+    rng = np.random.default_rng(32)
+    v = rng.standard_normal((3, 64)) * np.array([[1e-3], [1.0], [300.0]])
+    v[1, 5] = 0.0
+    codes, scales = oracle.mx8_quant(v)
+    grid = np.array([oracle.e4m3(c) for c in range(256) if c not in (0x7F, 0xFF)])
+    deq = oracle.mx8_dequant(codes, scales)
+    for r in range(3):
+        for b in range(2):
+            blk = v[r, 32 * b:32 * b + 32]
+            X = oracle.mx_scale(scales[r, b])
+            amax = np.abs(blk).max()
+            assert X == 2.0 ** (np.floor(np.log2(amax)) - 8)
+            for i in range(32):
+                dist = np.abs(grid * X - blk[i]).min()
+                assert abs(deq[r, 32 * b + i] - blk[i]) <= dist * (1 + 1e-12)
+    z = oracle.mx8_quant(np.zeros((1, 32)))
+    assert np.all(z[0] == 0) and z[1][0, 0] == 0
+
+
+def _tiny_mx():
+    sp = dict(T=5, H=128, I=128, E=3, k=2, router="normal", zipf=None)
+    L = synth.make_layer(sp, seed=33)
+    ex = oracle.Experts(**{n: v.numpy() for n, v in L["experts"].items()})
+    return sp, L, ex
+
+
+def test_nvfp4_to_mxfp8_is_the_quantiser_on_exact_weights():
+    """The requantised weights are MXFP8 of the exact NVFP4 weights (row by row), and every
+    value is a nearest point of its block's scaled e4m3 grid."""
+    sp, L, ex = _tiny_mx()
+    mx = oracle.nvfp4_to_mxfp8(ex)
+    grid = np.array([oracle.e4m3(c) for c in range(256) if c not in (0x7F, 0xFF)])
+    for m in range(3):
+        for e in range(ex.E):
+            W = oracle.dequant(ex, e, m)
+            q, s = (mx.gate_q, mx.up_q, mx.down_q)[m][e], (mx.gate_s, mx.up_s, mx.down_s)[m][e]
+            cq, cs = oracle.mx8_quant(W)
+            assert np.array_equal(q, cq) and np.array_equal(s, cs)
+            Wq = oracle.mx8_weights(mx, e, m)
+            for n in range(0, W.shape[0], 19):
+                for kk in range(0, W.shape[1], 7):
+                    X = oracle.mx_scale(s[n, kk // 32])
+                    dist = np.abs(grid * X - W[n, kk]).min()
+                    assert abs(Wq[n, kk] - W[n, kk]) <= dist * (1 + 1e-12)
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def test_expert_rows_mx_composition_and_planted_mistake():
+    """The fp8 expert FFN equals its pinned parts composed with numpy matmuls: MXFP8 x, MXFP8
+    weights, SwiGLU, MXFP8 h, down.  Leaving h unquantised (a plausible slip) is caught, and the
+    variant stays within its accuracy bar of the exact NVFP4 expert."""
+    sp, L, ex = _tiny_mx()
+    mx = oracle.nvfp4_to_mxfp8(ex)
+    xb = _bits(L["x"])
+    tok = np.array([0, 3, 4])
+    x = L["x"].double().numpy()[tok]
+    xq = oracle.mx8_dequant(*oracle.mx8_quant(x))
+    for e in range(ex.E):
+        Wg, Wu, Wd = (oracle.mx8_weights(mx, e, m) for m in range(3))
+        h = _silu(xq @ Wg.T) * (xq @ Wu.T)
+        hq = oracle.mx8_dequant(*oracle.mx8_quant(h))
+        want = hq @ Wd.T
+        got = oracle.expert_rows_mx(xb, mx, e, tok)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
+        slip = h @ Wd.T
+        assert not np.allclose(got, slip, rtol=1e-4, atol=0)
+        exact = oracle.expert_rows(xb, ex, e, tok)
+        assert np.linalg.norm(got - exact) <= 0.15 * np.linalg.norm(exact)
