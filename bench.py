@@ -36,12 +36,18 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/s + achieved HBM GB/s (T=1,64) / MFMA util (T=16K)"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense f16/bf16 matrix throughput
+MFMA_F8_PEAK_TFS = 5000.0   # MI355X dense fp8 matrix throughput
 POOL = 64
 
 
 def expert_bytes(H, I):
     """packed e2m1 codes + e4m3 scales of gate, up and down of one expert"""
     return 3 * (H * I // 2 + H * I // 16)
+
+
+def mx8_expert_bytes(H, I):
+    """e4m3 codes + e8m0 scales (one per 32) of gate, up and down of one expert"""
+    return 3 * (H * I + H * I // 32)
 
 
 def main():
@@ -54,6 +60,9 @@ def main():
     ap.add_argument("--combine", default="plain", choices=["plain", "norm"],
                     help="plain: routing-weighted sum; norm: per-expert RMS norm before the sum "
                          "and the residual + next pre-norm epilogue (four-call path)")
+    ap.add_argument("--precision", default="nvfp4", choices=["nvfp4", "mx8"],
+                    help="mx8: the fp8-compute variant (MXFP8 weights requantised from NVFP4 at "
+                         "load time, MXFP8 x and h, scaled matrix cores; four-call path)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle sample budget (0 disables the CPU baseline)")
     args = ap.parse_args()
@@ -79,7 +88,11 @@ def main():
     layer = synth.make_layer(sp, seed=0, device=dev, T=T * pool)
     xs = layer["x"]
     wr, bias = layer["w_router"], layer["bias"]
-    ex = moe.pack_experts(layer["experts"])  # tile-major copy (load-time conversion)
+    mx8 = args.precision == "mx8"
+    if mx8:  # load-time requantisation to MXFP8 (outside the timed region)
+        ex = moe.mx8_experts(layer["experts"])
+    else:
+        ex = moe.pack_experts(layer["experts"])  # tile-major copy (load-time conversion)
     buf = moe.LayerBuffers(T, H, I, E, k, device=dev, y_dtype=torch.float16, logits=False)
     torch.cuda.synchronize()
 
@@ -90,7 +103,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     # one or two tokens: the whole layer is one persistent kernel (plain combine only)
-    fused = T <= 2 and args.combine == "plain"
+    fused = T <= 2 and args.combine == "plain" and not mx8
     norm = args.combine == "norm"
     if norm:
         g = torch.Generator(device=dev)
@@ -115,8 +128,12 @@ def main():
                   buf.active, buf.n_active, buf.ws, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        moe.expert_ffn_nvfp4(x, ex, buf.count, buf.offset, buf.sorted_slot, buf.active,
-                             buf.n_active, k, buf.y, buf.ws, stream=stream)
+        if mx8:
+            moe.expert_ffn_mx8(x, ex, buf.count, buf.offset, buf.sorted_slot, buf.active,
+                               buf.n_active, k, buf.y, buf.ws, stream=stream)
+        else:
+            moe.expert_ffn_nvfp4(x, ex, buf.count, buf.offset, buf.sorted_slot, buf.active,
+                                 buf.n_active, k, buf.y, buf.ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         if evc is not None:
@@ -169,7 +186,7 @@ def main():
 
     ms_step = elapsed * 1e3 / steps
     tok_s = T * steps / elapsed
-    w_bytes = nd * expert_bytes(H, I)
+    w_bytes = nd * (mx8_expert_bytes(H, I) if mx8 else expert_bytes(H, I))
     ffn_bytes = w_bytes + T * H * 2 + T * k * H * 2          # weights + x + y (f16)
     layer_bytes = w_bytes + T * H * 2 + H * E * 4 + T * H * 4  # weights + x + router + out
     flops = 6.0 * T * k * H * I
@@ -179,13 +196,17 @@ def main():
         kernel, kbytes = "layer_small_kernel", layer_bytes
         if wl == "decode1":
             traffic = measured_traffic("traffic_layer_small_decode1.txt")
+    elif mx8:
+        kernel, kbytes = "fp8 expert FFN call (x quantiser + two scaled-MFMA grouped GEMMs)", ffn_bytes
+        traffic = measured_traffic("traffic_ffn_mx8_%s.txt" % wl)
     else:
         kernel, kbytes = "expert FFN call (few-row kernels + grouped GEMM)", ffn_bytes
         traffic = measured_traffic("traffic_ffn_%s.txt" % wl)
     if big:
+        peak = MFMA_F8_PEAK_TFS if mx8 else MFMA_F16_PEAK_TFS
         achieved = flops / (ffn_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_F16_PEAK_TFS,
-                    unit="TFLOP/s", frac=round(achieved / MFMA_F16_PEAK_TFS, 4), traffic=traffic,
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak,
+                    unit="TFLOP/s", frac=round(achieved / peak, 4), traffic=traffic,
                     kernel=kernel)
     else:
         achieved = kbytes / (ffn_ms * 1e-3) / 1e9
@@ -207,18 +228,22 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(layer, sp, pool, args.cpu_seconds)
+        cpu = (cpu_baseline_mx8(layer, sp, args.cpu_seconds) if mx8 else
+               cpu_baseline(layer, sp, pool, args.cpu_seconds))
         if norm:
             cpu["combine_norm"] = cpu_combine_norm(T, k, H, min(T, 256))
 
     res = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 (e4m3, MX)" if mx8 else "f16",
         "data": "synthetic",
         "config": {"workload": wl, "T": T, "H": H, "I": I, "E": E, "k": k,
                    "combine": "expert_norm+residual_norm" if norm else "plain",
-                   "weights": "nvfp4 (e2m1, e4m3 per 16, fp32 per matrix)",
+                   "weights": ("mxfp8 (e4m3, e8m0 per 32), requantised from nvfp4 at load"
+                               if mx8 else "nvfp4 (e2m1, e4m3 per 16, fp32 per matrix)"),
+                   "precision": args.precision,
                    "token_pool": pool, "seed": 0, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -278,6 +303,40 @@ def cpu_baseline(layer, sp, pool, budget_s):
             "kind": "oracle",
             "sample": "%d token(s) of the %s workload, whole layer per token (fp64 oracle)"
                       % (done, "decode" if pool > 1 else "same")}
+
+
+def cpu_baseline_mx8(layer, sp, budget_s):
+    """The oracle's fp8 variant on a bounded sample: per token, the oracle router and top-k, the
+    MXFP8 requantisation of that token's k experts, their fp8 FFN rows and the weighted sum;
+    tokens/s (the requantisation is counted: the oracle has no other way to get the weights)."""
+    import numpy as np
+    import oracle
+    print("copying inputs to the host for the CPU oracle (fp8 variant)", file=sys.stderr,
+          flush=True)
+    x = layer["x"].cpu().view(torch.int16).numpy().view(np.uint16)
+    wr = layer["w_router"].cpu().numpy()
+    bias = None if layer["bias"] is None else layer["bias"].cpu().numpy()
+    k = sp["k"]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        t = done % x.shape[0]
+        ids, w = oracle.topk(oracle.router(x[t:t + 1], wr, bias), k)
+        sub = oracle.Experts(**{n: v[ids[0].tolist()].cpu().numpy()
+                                for n, v in layer["experts"].items()})
+        mx = oracle.nvfp4_to_mxfp8(sub)
+        out = np.zeros(sp["H"])
+        for j in range(k):
+            out += w[0, j] * oracle.expert_rows_mx(x[t:t + 1], mx, j, [0])[0]
+        done += 1
+        if time.perf_counter() - t0 >= budget_s or done >= x.shape[0]:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 4), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d token(s) of the workload, fp8 variant per token (router, top-k, MXFP8 "
+                      "requantisation of its experts, fp8 FFN rows, weighted sum; fp64 oracle)"
+                      % done}
 
 
 def cpu_combine_norm(T, k, H, ntok):

@@ -29,6 +29,13 @@ class _Experts(ctypes.Structure):
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
 
 
+class _Mx8Experts(ctypes.Structure):
+    _fields_ = [("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p),
+                ("down_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
+                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+
 def lib():
     """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
     global _lib
@@ -62,13 +69,18 @@ def lib():
         L.moe_layer_nvfp4.restype = i32
         L.moe_layer_nvfp4.argtypes = [vp, vp, vp, ctypes.POINTER(_Experts), i32, i32, vp, vp,
                                       vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+        L.moe_nvfp4_to_mxfp8.restype = i32
+        L.moe_nvfp4_to_mxfp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_expert_ffn_mx8.restype = i32
+        L.moe_expert_ffn_mx8.argtypes = [vp, ctypes.POINTER(_Mx8Experts), vp, vp, vp, vp, vp,
+                                         i32, i32, vp, vp, sz, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
             "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_norm",
-            "moe_nvfp4_pack", "moe_layer_nvfp4")
+            "moe_nvfp4_pack", "moe_layer_nvfp4", "moe_nvfp4_to_mxfp8", "moe_expert_ffn_mx8")
 
 
 def abi_version():
@@ -198,6 +210,67 @@ def expert_ffn_nvfp4(x, experts, count, offset, sorted_slot, active, n_active, k
             _dev(y, "y", y.dtype, (T * k, H)), yd, _dev(ws, "ws", torch.uint8), ws.numel(),
             _stream(stream, x.device))
     _check(lib().moe_expert_ffn_nvfp4(*args), "moe_expert_ffn_nvfp4")
+
+
+_MATRIX = {"gate": 0, "up": 1, "down": 2}
+
+
+def nvfp4_to_mxfp8(q, s, ts, matrix, q8=None, s8=None, stream=None):
+    """moe_nvfp4_to_mxfp8: row-major NVFP4 codes q [E][N][K/2] and scales s [E][N][K/16]
+    (uint8), tensor scales ts [E][3] float32 and matrix "gate", "up" or "down" -> MXFP8 codes
+    q8 [E][N][K] and scales s8 [E][N][K/32] (uint8, new tensors unless given) in the tile
+    layout the fp8 FFN reads (the tensor shapes give sizes only)."""
+    E, N, k2 = q.shape
+    K = k2 * 2
+    if matrix not in _MATRIX:
+        raise ValueError("matrix must be gate, up or down")
+    if q8 is None:
+        q8 = torch.empty((E, N, K), dtype=torch.uint8, device=q.device)
+    if s8 is None:
+        s8 = torch.empty((E, N, K // 32), dtype=torch.uint8, device=q.device)
+    args = (_dev(q, "q", torch.uint8, (E, N, K // 2)), _dev(s, "s", torch.uint8, (E, N, K // 16)),
+            _dev(ts, "ts", torch.float32, (E, 3)), _MATRIX[matrix], E, N, K,
+            _dev(q8, "q8", torch.uint8, (E, N, K)), _dev(s8, "s8", torch.uint8, (E, N, K // 32)),
+            _stream(stream, q.device))
+    _check(lib().moe_nvfp4_to_mxfp8(*args), "moe_nvfp4_to_mxfp8")
+    return q8, s8
+
+
+def mx8_experts(experts, stream=None):
+    """MXFP8 copy (dict gate_q, up_q, down_q, gate_s, up_s, down_s) of a dict of ROW-MAJOR NVFP4
+    expert tensors (gate_q, up_q, down_q, gate_s, up_s, down_s, ts)."""
+    out = {}
+    for m in ("gate", "up", "down"):
+        out[m + "_q"], out[m + "_s"] = nvfp4_to_mxfp8(experts[m + "_q"], experts[m + "_s"],
+                                                      experts["ts"], m, stream=stream)
+    return out
+
+
+def mx8_struct(mx8):
+    """ctypes struct for a dict of MXFP8 expert tensors as mx8_experts returns."""
+    E, I, H = mx8["gate_q"].shape
+    shapes = dict(gate_q=(E, I, H), up_q=(E, I, H), down_q=(E, H, I),
+                  gate_s=(E, I, H // 32), up_s=(E, I, H // 32), down_s=(E, H, I // 32))
+    ptr = {n: _dev(mx8[n], n, torch.uint8, s) for n, s in shapes.items()}
+    return _Mx8Experts(ptr["gate_q"], ptr["up_q"], ptr["down_q"], ptr["gate_s"], ptr["up_s"],
+                       ptr["down_s"], E, H, I)
+
+
+def expert_ffn_mx8(x, mx8, count, offset, sorted_slot, active, n_active, k, y, ws, stream=None):
+    """moe_expert_ffn_mx8: y [T*k][H] float16 in grouped row order (fp8 compute)."""
+    T, H = x.shape
+    s = mx8_struct(mx8)
+    if s.H != H:
+        raise ValueError("x hidden size %d does not match experts %d" % (H, s.H))
+    E = s.E
+    args = (_dev(x, "x", torch.bfloat16), ctypes.byref(s), _dev(count, "count", torch.int32, (E,)),
+            _dev(offset, "offset", torch.int32, (E + 1,)),
+            _dev(sorted_slot, "sorted_slot", torch.int32, (T * k,)),
+            _dev(active, "active", torch.int32, (E,)),
+            _dev(n_active, "n_active", torch.int32, (1,)), T, k,
+            _dev(y, "y", torch.float16, (T * k, H)), _dev(ws, "ws", torch.uint8), ws.numel(),
+            _stream(stream, x.device))
+    _check(lib().moe_expert_ffn_mx8(*args), "moe_expert_ffn_mx8")
 
 
 def combine(y, slot_row, topk_w, out, stream=None):

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_nvfp4.so")
 SOURCES = ["api.hip", "route.hip", "group.hip", "ffn.hip", "combine.hip", "pack.hip", "gemm.hip",
-           "layer_small.hip", "combine_norm.hip"]
+           "layer_small.hip", "combine_norm.hip", "mx8.hip"]
 HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "dot.h"), os.path.join(ROOT, "include", "moe_nvfp4.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -29,6 +29,12 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   L.ffn_h16 = base + align_up((size_t)T * H * sizeof(_Float16), 256);
   L.ffn_tiles = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
   L.ffn_end = L.ffn_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
+  L.mx8_x8 = base;
+  L.mx8_xs = L.mx8_x8 + align_up((size_t)T * H, 256);
+  L.mx8_h8 = L.mx8_xs + align_up((size_t)T * H / 32, 256);
+  L.mx8_hs = L.mx8_h8 + align_up(n * I, 256);
+  L.mx8_tiles = L.mx8_hs + align_up(n * I / 32, 256);
+  L.mx8_end = L.mx8_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
   L.ls_partial = base;
   L.ls_h = base + align_up((size_t)32 * T * E * sizeof(float), 256);
   L.ls_end = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
@@ -36,6 +42,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   if (L.group_end > tot) tot = L.group_end;
   if (L.ffn_end > tot) tot = L.ffn_end;
   if (L.ls_end > tot) tot = L.ls_end;
+  if (L.mx8_end > tot) tot = L.mx8_end;
   L.total = tot;
   return L;
 }
@@ -285,4 +292,69 @@ MOE_API moe_status moe_nvfp4_pack(const uint8_t* q_rowmajor_dev, const uint8_t* 
   if (si < so + sbytes && so < si + sbytes) return MOE_ERR_INVALID_ARGUMENT;
   return from_hip(moe::launch_pack(q_rowmajor_dev, s_rowmajor_dev, E, N, K, q_tiled_dev,
                                    s_tiled_dev, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_nvfp4_to_mxfp8(const uint8_t* q_rowmajor_dev, const uint8_t* s_rowmajor_dev,
+                                      const float* tensor_scale_dev, int32_t matrix, int32_t E,
+                                      int32_t N, int32_t K, uint8_t* q8_dev, uint8_t* s8_dev,
+                                      void* stream) {
+  if (!q_rowmajor_dev || !s_rowmajor_dev || !tensor_scale_dev || !q8_dev || !s8_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q_rowmajor_dev, s_rowmajor_dev, tensor_scale_dev, q8_dev, s8_dev};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (matrix < 0 || matrix > 2 || E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > moe::kMaxExperts || N % 32 != 0 || K % 256 != 0 || N > 65536 || K > 65536)
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  const size_t qin = (size_t)E * N * K / 2, sin = (size_t)E * N * K / 16;
+  const size_t qout = (size_t)E * N * K, sout = (size_t)E * N * K / 32;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(q8_dev, qout, q_rowmajor_dev, qin) || overlap(q8_dev, qout, s_rowmajor_dev, sin) ||
+      overlap(s8_dev, sout, q_rowmajor_dev, qin) || overlap(s8_dev, sout, s_rowmajor_dev, sin) ||
+      overlap(q8_dev, qout, s8_dev, sout))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(moe::launch_nvfp4_to_mx8(q_rowmajor_dev, s_rowmajor_dev, tensor_scale_dev,
+                                           matrix, E, N, K, q8_dev, s8_dev,
+                                           (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_expert_ffn_mx8(const void* x_dev, const moe_mx8_experts* w,
+                                      const int32_t* count_dev, const int32_t* offset_dev,
+                                      const int32_t* sorted_slot_dev, const int32_t* active_dev,
+                                      const int32_t* n_active_dev, int32_t T, int32_t k,
+                                      void* y_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!x_dev || !w || !count_dev || !offset_dev || !sorted_slot_dev || !active_dev ||
+      !n_active_dev || !y_dev || !ws_dev)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->gate_q || !w->up_q || !w->down_q || !w->gate_s || !w->up_s || !w->down_s)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x_dev, count_dev, offset_dev, sorted_slot_dev, active_dev, n_active_dev,
+                        y_dev, ws_dev, w->gate_q, w->up_q, w->down_q, w->gate_s, w->up_s,
+                        w->down_s};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st != MOE_OK) return st;
+  if (w->H % 256 != 0 || w->I % 256 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
+  if (ws_bytes < L.mx8_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  moe::Mx8Args a;
+  a.x = (const uint16_t*)x_dev;
+  a.gq = w->gate_q; a.gs = w->gate_s; a.uq = w->up_q; a.us = w->up_s;
+  a.dq = w->down_q; a.ds = w->down_s;
+  a.count = count_dev; a.offset = offset_dev; a.sorted_slot = sorted_slot_dev;
+  a.active = active_dev; a.n_active = n_active_dev;
+  a.T = T; a.k = k; a.E = w->E; a.H = w->H; a.I = w->I;
+  a.y = (_Float16*)y_dev;
+  char* ws = (char*)ws_dev;
+  a.x8 = (uint8_t*)(ws + L.mx8_x8);
+  a.xs = (uint8_t*)(ws + L.mx8_xs);
+  a.h8 = (uint8_t*)(ws + L.mx8_h8);
+  a.hs = (uint8_t*)(ws + L.mx8_hs);
+  a.tiles = (int2*)(ws + L.mx8_tiles);
+  a.n_tiles = (int32_t*)(a.tiles + moe::gemm_max_tiles(T, k, w->E));
+  return from_hip(moe::launch_ffn_mx8(a, (hipStream_t)stream));
 }

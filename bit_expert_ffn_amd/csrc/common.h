@@ -45,6 +45,12 @@ struct WsLayout {
   size_t ffn_h16;        // [T*k][I] f16
   size_t ffn_tiles;      // busy-expert tile list: [gemm_max_tiles] int2, then the count (int32)
   size_t ffn_end;
+  size_t mx8_x8;         // fp8 variant: [T][H] e4m3 codes
+  size_t mx8_xs;         // [T][H/32] e8m0 scales
+  size_t mx8_h8;         // [T*k][I] e4m3 codes
+  size_t mx8_hs;         // [T*k][I/32] e8m0 scales
+  size_t mx8_tiles;      // tile list as ffn_tiles
+  size_t mx8_end;
   size_t ls_partial;     // single-launch layer: [32][T][E] fp32 router partials
   size_t ls_h;           // single-launch layer: [T*k][I] f16
   size_t ls_end;
@@ -75,6 +81,23 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
                            hipStream_t s);
 int gemm_rows_per_tile(int T);
 size_t gemm_max_tiles(int T, int k, int E);
+
+// fp8 variant of the expert FFN (mx8.hip): MXFP8 weights in the tile layout of the scaled
+// matrix cores, x and h quantised to MXFP8 on the fly, y in f16.
+struct Mx8Args {
+  const uint16_t* x;                           // [T][H] bf16
+  const uint8_t *gq, *gs, *uq, *us, *dq, *ds;  // MXFP8 tile layout
+  const int32_t *count, *offset, *sorted_slot, *active, *n_active;
+  int T, k, E, H, I;
+  _Float16* y;         // [T*k][H] grouped row order
+  uint8_t *x8, *xs;    // workspace
+  uint8_t *h8, *hs;    // workspace
+  int2* tiles;         // workspace
+  int32_t* n_tiles;    // workspace
+};
+hipError_t launch_ffn_mx8(const Mx8Args& a, hipStream_t s);
+hipError_t launch_nvfp4_to_mx8(const uint8_t* q, const uint8_t* s, const float* ts, int tsi,
+                               int E, int N, int K, uint8_t* q8, uint8_t* s8, hipStream_t st);
 
 // Single-launch layer for one or two tokens (layer_small.hip).
 constexpr int kLsMaxSlots = 32;  // most (token, slot) rows of the single-launch layer
@@ -118,6 +141,36 @@ struct CombineNormArgs {
   uint16_t* x_next;       // [T][H] bf16 (epilogue)
 };
 hipError_t launch_combine_norm(const CombineNormArgs& a, int y_f16, hipStream_t s);
+
+// List the MT-row tiles of every expert with >= min_rows rows (one wavefront).
+__device__ inline void ffn_plan(const int32_t* __restrict__ count, const int32_t* __restrict__ active,
+                         const int32_t* __restrict__ n_active, int MT, int min_rows,
+                         int2* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int na = *n_active;
+  int ex[4], nt[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = lane * 4 + i;
+    ex[i] = idx < na ? active[idx] : -1;
+    const int c = ex[i] >= 0 ? count[ex[i]] : 0;
+    nt[i] = c >= min_rows ? (c + MT - 1) / MT : 0;
+    sum += nt[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  int start = incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    for (int t = 0; t < nt[i] && start + t < max_tiles; ++t) tiles[start + t] = make_int2(ex[i], t * MT);
+    start += nt[i];
+  }
+  if (lane == 63) *n_tiles = incl < max_tiles ? incl : max_tiles;
+}
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

@@ -33,36 +33,6 @@ __device__ inline f16x8 gdecode8(uint32_t q, f16x2 s) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// List the MT-row tiles of every expert with >= min_rows rows (one wavefront).
-__device__ void ffn_plan(const int32_t* __restrict__ count, const int32_t* __restrict__ active,
-                         const int32_t* __restrict__ n_active, int MT, int min_rows,
-                         int2* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
-  const int lane = threadIdx.x & 63;
-  const int na = *n_active;
-  int ex[4], nt[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = lane * 4 + i;
-    ex[i] = idx < na ? active[idx] : -1;
-    const int c = ex[i] >= 0 ? count[ex[i]] : 0;
-    nt[i] = c >= min_rows ? (c + MT - 1) / MT : 0;
-    sum += nt[i];
-  }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
-  }
-  int start = incl - sum;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    for (int t = 0; t < nt[i] && start + t < max_tiles; ++t) tiles[start + t] = make_int2(ex[i], t * MT);
-    start += nt[i];
-  }
-  if (lane == 63) *n_tiles = incl < max_tiles ? incl : max_tiles;
-}
-
 // x [T][H] bf16 -> f16 (8 values per thread); block 0's first wavefront also builds the tile
 // list of the busy experts.
 __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(

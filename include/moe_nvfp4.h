@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 3
+#define MOE_NVFP4_ABI_VERSION 4
 
 typedef int32_t moe_status;
 enum {
@@ -228,6 +228,56 @@ moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const f
                            int32_t *active_dev, int32_t *n_active_dev, void *y_dev,
                            int32_t y_dtype, float *out_dev, void *ws_dev, size_t ws_bytes,
                            void *stream);
+
+/* ---- fp8-compute variant ------------------------------------------------------------------
+ * The pages' serving stack computes in fp8 with NVFP4 expert weights ("Optimizing Muse Spark
+ * Open on TPU v7 with SGLang-TorchTPU", Figure 1).  On gfx950 that runs on the scaled matrix
+ * cores in OCP MX form: MXFP8 = e4m3 (OCP E4M3FN) values with one e8m0 (power-of-two) scale
+ * per 32 consecutive values along the reduction.  Quantiser, per block of 32: E =
+ * floor(log2(max |v|)) - 8 clamped to [-127, 127] (an all-zero block gets E = -127 and zero
+ * codes); element code = e4m3 of v / 2^E, rounded to nearest with ties to even and saturated
+ * at 448; scale byte = E + 127.  This is an approximation of the layer, NOT the NVFP4 result:
+ * the weights are requantised (an NVFP4 weight has 1..4 significant bits times an e4m3 scale,
+ * which e4m3 under a shared power of two cannot always hold), and x and h are quantised.  On
+ * the pages' layer shapes with Gaussian inputs the expert outputs differ from the exact layer
+ * by about 7 % (relative L2); the variant is for callers that accept fp8 accuracy.
+ *
+ * MXFP8 expert weights.  Per expert e and matrix [N][K] (gate/up: N = I, K = H; down: N = H,
+ * K = I), with r = n / 32, st = kk / 64, b = kk / 32 (the 32-block), and within the block
+ * i = kk % 32:
+ *     code  byte of (n, kk): e*N*K + ((r*(K/64) + st)*64 + n%32 + 32*(i/16))*32 + 16*(b%2) + i%16
+ *     scale byte of (n, b):  e*N*K/32 + ((r*(K/256) + st/4)*64 + n%32 + 32*(b%2))*4 + st%4
+ * i.e. 32-row x 64-column tiles of 2 KB in which each of the 64 lanes of a wavefront finds the
+ * 32 bytes one matrix-core operand takes, and per 32-row tile and four 64-column steps 256
+ * bytes of scales, four per lane.  Sizes: codes E*N*K bytes, scales E*N*K/32 bytes. */
+typedef struct moe_mx8_experts {
+  const uint8_t *gate_q, *up_q, *down_q;
+  const uint8_t *gate_s, *up_s, *down_s;
+  int32_t E, H, I;
+} moe_mx8_experts;
+
+/* Load-time requantisation of one NVFP4 matrix kind (row-major input, as moe_nvfp4_pack takes:
+ * codes [E][N][K/2] with the low nibble holding the even k, scales [E][N][K/16]) to MXFP8 in
+ * the layout above.  tensor_scale_dev is [E][3] fp32 and `matrix` (0 gate, 1 up, 2 down)
+ * selects the column applied.  Every NVFP4 weight is dequantised exactly (in double) before
+ * the quantiser runs, so the result is deterministic.  Requires N % 32 == 0, K % 256 == 0,
+ * N, K <= 65536; outputs must not overlap the inputs.  Asynchronous on `stream`. */
+moe_status moe_nvfp4_to_mxfp8(const uint8_t *q_rowmajor_dev, const uint8_t *s_rowmajor_dev,
+                              const float *tensor_scale_dev, int32_t matrix, int32_t E,
+                              int32_t N, int32_t K, uint8_t *q8_dev, uint8_t *s8_dev,
+                              void *stream);
+
+/* Expert FFN in fp8 (same rows, grouping arrays and output order as moe_expert_ffn_nvfp4):
+ *   x8 = MXFP8(x) per token row; g = W8g.x8, u = W8u.x8 (products on the scaled matrix cores,
+ *   fp32 accumulation); h = g / (1 + exp(-g)) * u in fp32, h8 = MXFP8(h) per 32 features;
+ *   y = W8d.h8, written as f16 (y_dev [T*k][H] f16, grouped row order).
+ * Requires H % 256 == 0 and I % 256 == 0 besides the common limits.  ws_dev as for the other
+ * calls (moe_workspace_size). */
+moe_status moe_expert_ffn_mx8(const void *x_dev, const moe_mx8_experts *w,
+                              const int32_t *count_dev, const int32_t *offset_dev,
+                              const int32_t *sorted_slot_dev, const int32_t *active_dev,
+                              const int32_t *n_active_dev, int32_t T, int32_t k, void *y_dev,
+                              void *ws_dev, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

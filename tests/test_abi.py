@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     for code in (OK, INVALID, SHAPE, WS, -4, -5, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
 
@@ -167,6 +167,42 @@ def test_pack_rejects_bad_arguments():
     assert p(A, B, 2, 24, 128, C, D, None) == SHAPE
     assert p(A, B, 2, 16, 96, C, D, None) == SHAPE
     assert p(A, B, 2, 16, 128, A, D, None) == INVALID  # in place
+
+
+def test_nvfp4_to_mxfp8_rejects_bad_arguments():
+    f = moe.lib().moe_nvfp4_to_mxfp8
+    B, C, D, F = A + (1 << 40), A + (2 << 40), A + (3 << 40), A + (4 << 40)
+    assert f(None, B, C, 0, 2, 32, 256, D, F, None) == INVALID
+    assert f(A, B, None, 0, 2, 32, 256, D, F, None) == INVALID
+    assert f(A, B, C, 3, 2, 32, 256, D, F, None) == INVALID  # matrix
+    assert f(A, B, C, -1, 2, 32, 256, D, F, None) == INVALID
+    assert f(A, B, C, 0, 0, 32, 256, D, F, None) == INVALID
+    assert f(A, B, C, 0, 2, 32, 256, D + 8, F, None) == INVALID  # alignment
+    assert f(A, B, C, 0, 2, 16, 256, D, F, None) == SHAPE  # N % 32
+    assert f(A, B, C, 0, 2, 32, 128, D, F, None) == SHAPE  # K % 256
+    assert f(A, B, C, 0, 300, 32, 256, D, F, None) == SHAPE
+    assert f(A, B, C, 0, 2, 32, 256, A, F, None) == INVALID  # output over the input codes
+    assert f(A, B, C, 0, 2, 32, 256, D, B, None) == INVALID  # output over the input scales
+    assert f(A, B, C, 0, 2, 32, 256, D, D + 256, None) == INVALID  # outputs overlap
+
+
+def _mx8(**over):
+    a = dict(x=A, ex=moe._Mx8Experts(A, A, A, A, A, A, 8, 256, 256), T=4, k=2, y=A, ws=A,
+             ws_bytes=1 << 30)
+    a.update(over)
+    return moe.lib().moe_expert_ffn_mx8(a["x"], ctypes.byref(a["ex"]), A, A, A, A, A, a["T"],
+                                        a["k"], a["y"], a["ws"], a["ws_bytes"], None)
+
+
+def test_expert_ffn_mx8_rejects_bad_arguments():
+    assert _mx8(x=None) == INVALID
+    assert _mx8(y=A + 2) == INVALID
+    assert _mx8(ex=moe._Mx8Experts(A, None, A, A, A, A, 8, 256, 256)) == INVALID
+    assert _mx8(T=0) == INVALID
+    assert _mx8(k=9) == INVALID
+    assert _mx8(ex=moe._Mx8Experts(A, A, A, A, A, A, 8, 384, 256)) == SHAPE  # H % 256
+    assert _mx8(ex=moe._Mx8Experts(A, A, A, A, A, A, 8, 256, 128)) == SHAPE  # I % 256
+    assert _mx8(ws_bytes=1024) == WS
 
 
 def _layer(**over):
