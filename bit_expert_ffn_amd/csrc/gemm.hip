@@ -119,7 +119,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
   const int N = GATEUP ? I : H;  // rows of one weight matrix
   const int nchunk = K / 128;
   const int nstage = K / gK;
-  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
 
   // activation rows of this thread's pieces (rows past the expert's end repeat its last row:
   // their outputs are never stored).  Offsets are 32-bit element offsets from a uniform base
@@ -208,8 +209,9 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const f16x8 a = *reinterpret_cast<const f16x8*>(&As[buf][i * 32 + r32][hgrp * 32 + step * 8]);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[i][1], 0, 0, 0);
+        // weights first: the accumulator holds the transposed tile (see the epilogue)
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, a, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, a, acc[i][1], 0, 0, 0);
       }
     }
   };
@@ -245,43 +247,57 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     }
   }
 
-  // epilogue; accumulator element v of a 32x32 tile: row (v/4)*8 + (lane/32)*4 + v%4, col lane%32
-  const int rm = hgrp;
+  // epilogue.  With the weights as the first operand, element v of lane l of a 32x32
+  // accumulator is row (token) l % 32 of the sub-tile and feature (v / 4) * 8 + (l / 32) * 4 +
+  // v % 4 of the weight tile: every lane holds four runs of four consecutive features of one
+  // row, stored as 8-byte (f16) or 16-byte (fp32) vectors.
   if (GATEUP) {
     const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
     _Float16* h16 = reinterpret_cast<_Float16*>(out);
-    const int f = feat[0];  // the gate tile and the up tile hold the same features
+    const int f0 = feat[0] - r32;  // first feature of the gate tile (= of the up tile)
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = m0 + i * 32 + r32;
+      if (m < rows && f0 < I) {
+        _Float16* dst = h16 + (size_t)(base + m) * I + f0 + hgrp * 4;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
-        if (m < rows && f < I) {
-          const float gv = acc[i][0][v] * tsg, uv = acc[i][1][v] * tsu;
-          h16[(size_t)(base + m) * I + f] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f16x4 o;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float gv = acc[i][0][4 * g4 + c] * tsg, uv = acc[i][1][4 * g4 + c] * tsu;
+            o[c] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+          }
+          *reinterpret_cast<f16x4*>(dst + 8 * g4) = o;
         }
       }
+    }
   } else {
     const float tsd = ts[e * 3 + 2];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = m0 + i * 32 + r32;
+      if (m >= rows) continue;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int f = feat[t];
-        if (f >= N) continue;
+        const int f0 = feat[t] - r32;
+        if (f0 >= N) continue;  // N is a multiple of 32: a tile is wholly in or out
+        const size_t o = (size_t)(base + m) * H + f0 + hgrp * 4;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + i * 32 + (v >> 2) * 8 + rm * 4 + (v & 3);
-          if (m < rows) {
-            const float yv = acc[i][t][v] * tsd;
-            const size_t o = (size_t)(base + m) * H + f;
-            if (Y_F16)
-              reinterpret_cast<_Float16*>(out)[o] = (_Float16)yv;
-            else
-              reinterpret_cast<float*>(out)[o] = yv;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          if (Y_F16) {
+            const f16x4 v = {(_Float16)(acc[i][t][4 * g4] * tsd), (_Float16)(acc[i][t][4 * g4 + 1] * tsd),
+                             (_Float16)(acc[i][t][4 * g4 + 2] * tsd),
+                             (_Float16)(acc[i][t][4 * g4 + 3] * tsd)};
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(out) + o + 8 * g4) = v;
+          } else {
+            const f32x4 v = {acc[i][t][4 * g4] * tsd, acc[i][t][4 * g4 + 1] * tsd,
+                             acc[i][t][4 * g4 + 2] * tsd, acc[i][t][4 * g4 + 3] * tsd};
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o + 8 * g4) = v;
           }
         }
       }
+    }
   }
 }
 

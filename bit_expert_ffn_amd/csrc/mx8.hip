@@ -226,7 +226,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
   const int K = GATEUP ? H : I;
   const int N = GATEUP ? I : H;
   const int nst = K / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31, hh = lane >> 5;
 
   // this thread's activation piece: row tid / 4 of the tile, bytes 16 (tid % 4) of each step;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row0 = GATEUP ? fb * (32 * NW) + wn * 32 : fb * (64 * NW) + wn * 64 + t * 32;
-    feat[t] = row0 + r32;
+    feat[t] = row0;  // first feature of the tile
     const int tile = min(row0, N - 32) / 32;
     const size_t tix = (size_t)e * (N / 32) + tile;
     const uint8_t* qm = GATEUP && t == 1 ? q1 : q0;
@@ -304,8 +305,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
       const int sa = (int)((Ass[buf][row] >> (8 * hh)) & 0xffu);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        acc[i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, b[t], acc[i][t], 0, 0, 0,
-                                                                    sa, jj, (int)r.sd[t]);
+        acc[i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[t], av, acc[i][t], 0, 0, jj,
+                                                                    (int)r.sd[t], 0, sa);
     }
   };
 
@@ -314,11 +315,18 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
   // scale dword, is a compile-time constant.  Loads past the last step re-read it (unused).
   Stage rs[2];
   const int last = nst - 1;
+  // the prologue issues its loads in the loop's order (set 0, then set 1), so that the wait
+  // counts the compiler derives at the loop head stay those of the steady state
   load(rs[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
   load(rs[1], min(1, last));
+  __builtin_amdgcn_sched_barrier(0);
   store_a(rs[0], 0);
   lds_barrier();
-  for (int st = 0; st < nst; st += 4) {
+  // K >= 256 (checked by the caller): at least one pass, no guard branch for the compiler to
+  // sink the prologue loads into
+  int st = 0;
+  do {
 #define MOE_MX8_STEP(JJ)                                               \
     compute(rs[JJ & 1], JJ & 1, std::integral_constant<int, JJ>{});   \
     __builtin_amdgcn_sched_barrier(0);                                \
@@ -330,45 +338,61 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     MOE_MX8_STEP(2)
     MOE_MX8_STEP(3)
 #undef MOE_MX8_STEP
-  }
+    st += 4;
+  } while (st < nst);
 
-  // epilogue; accumulator element v of a 32x32 tile: row (v/4)*8 + (lane/32)*4 + v%4, column
-  // lane % 32
+  // epilogue.  The weights are the first operand, so each 32x32 accumulator is the transposed
+  // tile: element v of lane l is row (token) l % 32 of the sub-tile and feature
+  // (v / 4) * 8 + (l / 32) * 4 + v % 4 of the weight tile, i.e. every lane holds four runs of
+  // four consecutive features of one row.
   if (GATEUP) {
     uint8_t* h8 = reinterpret_cast<uint8_t*>(out);
-    const int f = feat[0];  // the gate tile and the up tile hold the same 32 features
+    const int f0 = feat[0];  // the gate tile and the up tile hold the same 32 features
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = m0 + i * 32 + r32;
+      float hv[16], amax = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
         const float g = acc[i][0][v], u = acc[i][1][v];
-        const float hv = g / (1.0f + expf(-g)) * u;
-        // MXFP8 block: this row's 32 features, held by the 32 lanes of this half-wavefront
-        float amax = fabsf(hv);
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-        const int E = mx8_exp(amax);
-        const uint32_t code = amax > 0.f ? e4m3_pack4(ldexpf(hv, -E), 0.f, 0.f, 0.f) & 0xffu : 0u;
-        if (m < rows && f < N) {
-          h8[(size_t)(base + m) * I + f] = (uint8_t)code;
-          if (r32 == 0) hs_out[(size_t)(base + m) * (I / 32) + f / 32] = (uint8_t)(E + 127);
-        }
+        hv[v] = g / (1.0f + expf(-g)) * u;
+        amax = fmaxf(amax, fabsf(hv[v]));
       }
+      // the row's MXFP8 block: its 32 features, 16 in this lane and 16 in lane l ^ 32
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const int E = mx8_exp(amax);
+      if (m < rows && f0 < N) {
+        uint8_t* dst = h8 + (size_t)(base + m) * I + f0 + hh * 4;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const uint32_t w = amax > 0.f ? e4m3_pack4(ldexpf(hv[4 * g4], -E), ldexpf(hv[4 * g4 + 1], -E),
+                                                     ldexpf(hv[4 * g4 + 2], -E),
+                                                     ldexpf(hv[4 * g4 + 3], -E))
+                                        : 0u;
+          *reinterpret_cast<uint32_t*>(dst + 8 * g4) = w;
+        }
+        if (hh == 0) hs_out[(size_t)(base + m) * (I / 32) + f0 / 32] = (uint8_t)(E + 127);
+      }
+    }
   } else {
     _Float16* y = reinterpret_cast<_Float16*>(out);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = m0 + i * 32 + r32;
+      if (m >= rows) continue;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int f = feat[t];
-        if (f >= N) continue;
+        const int f0 = feat[t];
+        if (f0 >= N) continue;  // N is a multiple of 32: a tile is wholly in or out
+        _Float16* dst = y + (size_t)(base + m) * H + f0 + hh * 4;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
-          if (m < rows) y[(size_t)(base + m) * H + f] = (_Float16)acc[i][t][v];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f16x4 o = {(_Float16)acc[i][t][4 * g4], (_Float16)acc[i][t][4 * g4 + 1],
+                           (_Float16)acc[i][t][4 * g4 + 2], (_Float16)acc[i][t][4 * g4 + 3]};
+          *reinterpret_cast<f16x4*>(dst + 8 * g4) = o;
         }
       }
+    }
   }
 }
 
