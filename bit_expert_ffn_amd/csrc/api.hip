@@ -28,13 +28,13 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   L.ffn_x16 = base;
   L.ffn_h16 = base + align_up((size_t)T * H * sizeof(_Float16), 256);
   L.ffn_tiles = L.ffn_h16 + align_up(n * I * sizeof(_Float16), 256);
-  L.ffn_end = L.ffn_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
+  L.ffn_end = L.ffn_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int4) + sizeof(int32_t), 256);
   L.mx8_x8 = base;
   L.mx8_xs = L.mx8_x8 + align_up((size_t)T * H, 256);
   L.mx8_h8 = L.mx8_xs + align_up((size_t)T * H / 32, 256);
   L.mx8_hs = L.mx8_h8 + align_up(n * I, 256);
   L.mx8_tiles = L.mx8_hs + align_up(n * I / 32, 256);
-  L.mx8_end = L.mx8_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int2) + sizeof(int32_t), 256);
+  L.mx8_end = L.mx8_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int4) + sizeof(int32_t), 256);
   L.ls_partial = base;
   L.ls_h = base + align_up((size_t)32 * T * E * sizeof(float), 256);
   L.ls_end = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
@@ -164,7 +164,7 @@ MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_exper
   a.y_f16 = y_dtype == MOE_F16;
   a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
   a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
-  int2* tiles = reinterpret_cast<int2*>((char*)ws_dev + L.ffn_tiles);
+  int4* tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn(a, tiles, n_tiles, (hipStream_t)stream));
 }
@@ -354,7 +354,7 @@ MOE_API moe_status moe_expert_ffn_mx8(const void* x_dev, const moe_mx8_experts* 
   a.xs = (uint8_t*)(ws + L.mx8_xs);
   a.h8 = (uint8_t*)(ws + L.mx8_h8);
   a.hs = (uint8_t*)(ws + L.mx8_hs);
-  a.tiles = (int2*)(ws + L.mx8_tiles);
+  a.tiles = (int4*)(ws + L.mx8_tiles);
   a.n_tiles = (int32_t*)(a.tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn_mx8(a, (hipStream_t)stream));
 }

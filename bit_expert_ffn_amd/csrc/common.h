@@ -43,7 +43,7 @@ struct WsLayout {
   size_t group_end;
   size_t ffn_x16;        // [T][H] f16
   size_t ffn_h16;        // [T*k][I] f16
-  size_t ffn_tiles;      // busy-expert tile list: [gemm_max_tiles] int2, then the count (int32)
+  size_t ffn_tiles;      // busy-expert tile list: [gemm_max_tiles] int4, then the count (int32)
   size_t ffn_end;
   size_t mx8_x8;         // fp8 variant: [T][H] e4m3 codes
   size_t mx8_xs;         // [T][H/32] e8m0 scales
@@ -76,8 +76,8 @@ struct FfnArgs {
   _Float16* x16;  // workspace
   _Float16* h16;  // workspace
 };
-hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream_t s);
-hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t* n_tiles,
+hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream_t s);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t* n_tiles,
                            hipStream_t s);
 int gemm_rows_per_tile(int T);
 size_t gemm_max_tiles(int T, int k, int E);
@@ -92,7 +92,7 @@ struct Mx8Args {
   _Float16* y;         // [T*k][H] grouped row order
   uint8_t *x8, *xs;    // workspace
   uint8_t *h8, *hs;    // workspace
-  int2* tiles;         // workspace
+  int4* tiles;         // workspace: tile descriptors
   int32_t* n_tiles;    // workspace
 };
 hipError_t launch_ffn_mx8(const Mx8Args& a, hipStream_t s);
@@ -142,19 +142,25 @@ struct CombineNormArgs {
 };
 hipError_t launch_combine_norm(const CombineNormArgs& a, int y_f16, hipStream_t s);
 
-// List the MT-row tiles of every expert with >= min_rows rows (one wavefront).
-__device__ inline void ffn_plan(const int32_t* __restrict__ count, const int32_t* __restrict__ active,
-                         const int32_t* __restrict__ n_active, int MT, int min_rows,
-                         int2* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
+// List the MT-row tiles of every expert with >= min_rows rows (one wavefront).  Every tile
+// of expert e gets the same descriptor {e, index of e's first tile, rows of e, first grouped
+// row of e}: a tile's own first row is (its index - the first index) * MT, and the expert's
+// tiles are consecutive in the list.
+__device__ inline void ffn_plan(const int32_t* __restrict__ count,
+                                const int32_t* __restrict__ offset,
+                                const int32_t* __restrict__ active,
+                                const int32_t* __restrict__ n_active, int MT, int min_rows,
+                                int4* __restrict__ tiles, int max_tiles,
+                                int32_t* __restrict__ n_tiles) {
   const int lane = threadIdx.x & 63;
   const int na = *n_active;
-  int ex[4], nt[4], sum = 0;
+  int ex[4], nt[4], cnt[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = lane * 4 + i;
     ex[i] = idx < na ? active[idx] : -1;
-    const int c = ex[i] >= 0 ? count[ex[i]] : 0;
-    nt[i] = c >= min_rows ? (c + MT - 1) / MT : 0;
+    cnt[i] = ex[i] >= 0 ? count[ex[i]] : 0;
+    nt[i] = cnt[i] >= min_rows ? (cnt[i] + MT - 1) / MT : 0;
     sum += nt[i];
   }
   int incl = sum;
@@ -166,7 +172,10 @@ __device__ inline void ffn_plan(const int32_t* __restrict__ count, const int32_t
   int start = incl - sum;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    for (int t = 0; t < nt[i] && start + t < max_tiles; ++t) tiles[start + t] = make_int2(ex[i], t * MT);
+    if (nt[i] > 0) {
+      const int4 d = make_int4(ex[i], start, cnt[i], offset[ex[i]]);
+      for (int t = 0; t < nt[i] && start + t < max_tiles; ++t) tiles[start + t] = d;
+    }
     start += nt[i];
   }
   if (lane == 63) *n_tiles = incl < max_tiles ? incl : max_tiles;

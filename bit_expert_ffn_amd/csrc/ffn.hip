@@ -278,7 +278,7 @@ static int few_rows(int T, int H, int I) {
   return R;
 }
 
-hipError_t launch_ffn(const FfnArgs& a, int2* tiles, int32_t* n_tiles, hipStream_t s) {
+hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream_t s) {
   const int maxe = a.E < a.T * a.k ? a.E : a.T * a.k;
   const int R = few_rows(a.T, a.H, a.I);
   const bool heavy = a.T > R;  // some expert may have more than R rows

@@ -9,7 +9,7 @@
 //
 // Work list: ffn_plan (run by the first block of the activation-conversion kernel) walks the
 // active experts in order and lists every tile of MT rows of every expert with at least
-// min_rows rows: (expert, first row).  grid.y runs over a host-side bound of that list; blocks
+// min_rows rows, each with its expert's descriptor (expert, first tile, rows, first row).  grid.y runs over a host-side bound of that list; blocks
 // past its end return.  Nothing is read back by the host.
 //
 // Arithmetic: activations (x or h) and decoded weights enter v_mfma_f32_32x32x16_f16 as f16;
@@ -22,7 +22,6 @@ namespace moe {
 constexpr int gK = 64;       // K per pipeline stage
 constexpr int gLD = gK + 8;  // padded LDS row, in halves
 constexpr int kXcds = 8;     // MI355X: 8 accelerator dies (XCDs), workgroups dealt round-robin
-constexpr int kGroup = 4;    // consecutive row tiles whose blocks are ordered together
 constexpr int kGemmSets = 4;  // register sets of the load pipeline
 
 __device__ inline f16x8 gdecode8(uint32_t q, f16x2 s) {
@@ -37,9 +36,9 @@ __device__ inline f16x8 gdecode8(uint32_t q, f16x2 s) {
 // list of the busy experts.
 __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     const uint16_t* __restrict__ x, _Float16* __restrict__ x16, size_t n8,
-    const int32_t* __restrict__ count, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, int MT, int min_rows, int2* __restrict__ tiles,
-    int max_tiles, int32_t* __restrict__ n_tiles) {
+    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int MT,
+    int min_rows, int4* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n8) {
     const uint4 v = reinterpret_cast<const uint4*>(x)[i];
@@ -53,7 +52,7 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     reinterpret_cast<f16x8*>(x16)[i] = o;
   }
   if (blockIdx.x == 0 && threadIdx.x < 64)
-    ffn_plan(count, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
+    ffn_plan(count, offset, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
 // Block: NW wavefronts side by side in N; MT = 64 * WM rows x 64 NW weight rows; K in stages of
@@ -77,8 +76,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
-    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ sorted_slot, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ sorted_slot, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out) {
   constexpr int NTH = 64 * NW;      // threads per block
   constexpr int MT = 64 * WM;
@@ -88,10 +86,11 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;  // native vector: stays in VGPRs
   __shared__ __attribute__((aligned(16))) _Float16 As[2][MT][gLD];
   // Block order.  Workgroups go round-robin to the 8 XCDs, each with its own L2; renumber so
-  // that every XCD gets one contiguous range of the logical order, and in that order take
-  // groups of kGroup consecutive row tiles (about one expert), then the weight blocks, then the
-  // tiles of the group.  The blocks resident on one XCD then share a few activation tiles and
-  // a few weight slices.
+  // that every XCD gets one contiguous range of the logical order.  The logical order takes
+  // the experts one after another (their tiles are consecutive in the list) and, inside an
+  // expert, the weight blocks one after another and for each the expert's row tiles: the
+  // blocks that run together on an XCD are the row tiles of one expert against the same
+  // weight slice, which is then read from HBM about once.
   const int NB = gridDim.x;  // weight blocks
   const int ntl = *n_tiles;
   const int total = NB * ntl;
@@ -103,18 +102,13 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     const int per = total / kXcds, rem = total % kXcds;
     L = q * per + min(q, rem) + loc;
   }
-  int j, fb;
-  {
-    const int grp = L / (kGroup * NB);
-    const int gsz = min(kGroup, ntl - grp * kGroup);
-    const int within = L - grp * kGroup * NB;
-    fb = within / gsz;
-    j = grp * kGroup + within % gsz;
-  }
-  const int2 te = tiles[j];
-  const int e = te.x, m0 = te.y;
-  const int rows = count[e];
-  const int base = offset[e];
+  // expert e owns items [NB j0, NB (j0 + ne)), so tile L / NB is one of its tiles
+  const int4 td = tiles[L / NB];
+  const int e = td.x, rows = td.z, base = td.w;
+  const int ne = (rows + MT - 1) / MT;
+  const int o = L - NB * td.y;
+  const int fb = o / ne;
+  const int m0 = (o - fb * ne) * MT;
   const int K = GATEUP ? H : I;  // reduction length
   const int N = GATEUP ? I : H;  // rows of one weight matrix
   const int nchunk = K / 128;
@@ -310,13 +304,14 @@ size_t gemm_max_tiles(int T, int k, int E) {
   return n / MT + 1 + ne;
 }
 
-hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t* n_tiles,
+hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t* n_tiles,
                            hipStream_t s) {
   const int MT = gemm_rows_per_tile(a.T);
   const int max_tiles = (int)gemm_max_tiles(a.T, a.k, a.E);
   const size_t n8 = (size_t)a.T * a.H / 8;
   x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
-      a.x, a.x16, n8, a.count, a.active, a.n_active, MT, min_rows, tiles, max_tiles, n_tiles);
+      a.x, a.x16, n8, a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles, max_tiles,
+      n_tiles);
   // 128-row tiles: 8 wavefronts (512 weight rows per block); 64-row tiles (fewer rows, fewer
   // blocks): 4 wavefronts
 #define MOE_GEMM(GU_, WM_, F16_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
@@ -325,7 +320,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int2* tiles, int32_t*
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
     ffn_gemm_kernel<GU_, WM_, F16_, kGemmSets, NW_><<<g_, 64 * NW_, 0, s>>>(                  \
-        XA_, Q0_, S0_, Q1_, S1_, a.ts, a.count, a.offset, a.sorted_slot, tiles, n_tiles, a.k,  \
+        XA_, Q0_, S0_, Q1_, S1_, a.ts, a.sorted_slot, tiles, n_tiles, a.k,                     \
         a.H, a.I, OUT_);                                                                      \
   } while (0)
   if (MT == 128) {

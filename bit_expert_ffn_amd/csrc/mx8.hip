@@ -133,9 +133,9 @@ hipError_t launch_nvfp4_to_mx8(const uint8_t* q, const uint8_t* s, const float* 
 // 0's first wavefront also lists the tiles of every active expert.
 __global__ __launch_bounds__(256) void x_to_mx8_plan_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, uint8_t* __restrict__ xs,
-    size_t nblk, const int32_t* __restrict__ count, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, int MT, int2* __restrict__ tiles, int max_tiles,
-    int32_t* __restrict__ n_tiles) {
+    size_t nblk, const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int MT,
+    int4* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < nblk) {
     const uint4* src = reinterpret_cast<const uint4*>(x) + i * 4;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void x_to_mx8_plan_kernel(
     xs[i] = (uint8_t)(E + 127);
   }
   if (blockIdx.x == 0 && threadIdx.x < 64)
-    ffn_plan(count, active, n_active, MT, 1, tiles, max_tiles, n_tiles);
+    ffn_plan(count, offset, active, n_active, MT, 1, tiles, max_tiles, n_tiles);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -182,8 +182,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     const uint8_t* __restrict__ a8, const uint8_t* __restrict__ as8,
     const uint8_t* __restrict__ q0, const uint8_t* __restrict__ s0,
     const uint8_t* __restrict__ q1, const uint8_t* __restrict__ s1,
-    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
-    const int32_t* __restrict__ sorted_slot, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ sorted_slot, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out,
     uint8_t* __restrict__ hs_out) {
   constexpr int NTH = 64 * NW;
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
   __shared__ __attribute__((aligned(4))) uint16_t Ass[2][NTH];  // entries >= MT unused
 
   // block order: as in the NVFP4 grouped GEMM (one contiguous range of the logical order per
-  // XCD; groups of row tiles, then weight blocks)
+  // XCD; experts one after another, in each the weight blocks, in each the expert's row tiles)
   const int NB = gridDim.x;
   const int ntl = *n_tiles;
   const int total = NB * ntl;
@@ -210,19 +209,12 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     const int per = total / kX, rem = total % kX;
     L = qx * per + min(qx, rem) + loc;
   }
-  int j, fb;
-  {
-    constexpr int kG = 4;
-    const int grp = L / (kG * NB);
-    const int gsz = min(kG, ntl - grp * kG);
-    const int within = L - grp * kG * NB;
-    fb = within / gsz;
-    j = grp * kG + within % gsz;
-  }
-  const int2 te = tiles[j];
-  const int e = te.x, m0 = te.y;
-  const int rows = count[e];
-  const int base = offset[e];
+  const int4 td = tiles[L / NB];
+  const int e = td.x, rows = td.z, base = td.w;
+  const int ne = (rows + MT - 1) / MT;
+  const int o = L - NB * td.y;
+  const int fb = o / ne;
+  const int m0 = (o - fb * ne) * MT;
   const int K = GATEUP ? H : I;
   const int N = GATEUP ? I : H;
   const int nst = K / 64;
@@ -401,14 +393,15 @@ hipError_t launch_ffn_mx8(const Mx8Args& a, hipStream_t s) {
   const int max_tiles = (int)gemm_max_tiles(a.T, a.k, a.E);
   const size_t nblk = (size_t)a.T * a.H / 32;
   x_to_mx8_plan_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(
-      a.x, a.x8, a.xs, nblk, a.count, a.active, a.n_active, MT, a.tiles, max_tiles, a.n_tiles);
+      a.x, a.x8, a.xs, nblk, a.count, a.offset, a.active, a.n_active, MT, a.tiles, max_tiles,
+      a.n_tiles);
 #define MOE_MX8(GU_, WM_, A8_, AS_, Q0_, S0_, Q1_, S1_, OUT_, HS_)                             \
   do {                                                                                        \
     constexpr int NW_ = WM_ == 2 ? 8 : 4;                                                     \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
     mx8_gemm_kernel<GU_, WM_, NW_><<<g_, 64 * NW_, 0, s>>>(                                   \
-        A8_, AS_, Q0_, S0_, Q1_, S1_, a.count, a.offset, a.sorted_slot, a.tiles, a.n_tiles,    \
+        A8_, AS_, Q0_, S0_, Q1_, S1_, a.sorted_slot, a.tiles, a.n_tiles,                      \
         a.k, a.H, a.I, OUT_, HS_);                                                            \
   } while (0)
   if (MT == 128) {
