@@ -18,6 +18,8 @@
 // 1.0); the e4m3 block scale multiplies each 16-value block sum in fp32; the fp32 tensor scale
 // multiplies the final sum once.
 // Activations: x is dotted as bf16 (exact); h is stored as f16 (the down projection's input).
+#include <mutex>
+
 #include "common.h"
 #include "dot.h"
 
@@ -282,10 +284,52 @@ static int few_rows(int T, int H, int I) {
   return R;
 }
 
+// A second stream per device for the busy experts' chain (x -> f16 + plan, grouped GEMMs).  It
+// shares no data with the few-row chain (disjoint experts, so disjoint rows of h and y, and its
+// own workspace regions), so the two run side by side and the caller's stream waits for both.
+// Created once per device with the default priority; work of calls from several threads
+// queues on it in order.
+static hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    err = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (err != hipSuccess) {
+      streams[dev] = nullptr;
+      return err;
+    }
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream_t s) {
   const int maxe = a.E < a.T * a.k ? a.E : a.T * a.k;
   const int R = few_rows(a.T, a.H, a.I);
   const bool heavy = a.T > R;  // some expert may have more than R rows
+  // both paths present: fork the busy chain onto the side stream, launched first so that its
+  // blocks start alongside the few-row kernels
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t side = nullptr;
+  if (R > 0 && heavy) {
+    hipError_t err = side_stream(&side);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&ev_join, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventRecord(ev_fork, s);
+    if (err == hipSuccess) err = hipStreamWaitEvent(side, ev_fork, 0);
+    if (err == hipSuccess) err = launch_ffn_gemm(a, R + 1, tiles, n_tiles, side);
+    if (err == hipSuccess) err = hipEventRecord(ev_join, side);
+    if (err != hipSuccess) {
+      if (ev_fork) (void)hipEventDestroy(ev_fork);
+      if (ev_join) (void)hipEventDestroy(ev_join);
+      return err;
+    }
+  }
   // with few tokens nearly every expert is few-row: request weights before checking the count
   const int early = (size_t)a.T * a.k <= (size_t)4 * a.E ? 1 : 0;
   // gate/up + SwiGLU
@@ -338,6 +382,13 @@ hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream
 #undef MOE_FEW_D
   }
   hipError_t err = hipGetLastError();
+  if (side) {
+    // join: the caller's stream continues once the busy chain is done as well
+    const hipError_t werr = hipStreamWaitEvent(s, ev_join, 0);
+    (void)hipEventDestroy(ev_fork);
+    (void)hipEventDestroy(ev_join);
+    return err != hipSuccess ? err : werr;
+  }
   if (err != hipSuccess) return err;
   if (heavy) return launch_ffn_gemm(a, R + 1, tiles, n_tiles, s);
   return hipGetLastError();
