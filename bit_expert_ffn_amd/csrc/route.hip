@@ -51,7 +51,10 @@ RoutePlan route_plan(int T, int H, int E) {
     return p;
   }
   p.mfma = false;
-  p.TT = T <= 1 ? 1 : T <= 4 ? 4 : T <= 64 ? 8 : 16;
+  // 4-token tiles on 8 wavefronts from 2 tokens up: two wavefronts per SIMD hide the LDS and
+  // load latency of the FMA loop (measured faster than 8- or 16-token tiles on 4 wavefronts at
+  // 64 and 128 tokens)
+  p.TT = T <= 1 ? 1 : 4;
   p.RG = p.TT <= 4 ? 8 : 4;
   const int tiles = (T + p.TT - 1) / p.TT;
   int kc;
@@ -377,12 +380,10 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
       router_slices_kernel<TT_, RG_, false><<<grid, RG_ * 64, 0, s>>>(x, wr, T, H, E, p.kc,  \
                                                                       partial);               \
   } while (0)
-  switch (p.TT) {
-    case 1: MOE_SLICES(1, 8); break;
-    case 4: MOE_SLICES(4, 8); break;
-    case 8: MOE_SLICES(8, 4); break;
-    default: MOE_SLICES(16, 4); break;
-  }
+  if (p.TT == 1)
+    MOE_SLICES(1, 8);
+  else
+    MOE_SLICES(4, 8);
 #undef MOE_SLICES
   }
   if (p.KS >= 8)
