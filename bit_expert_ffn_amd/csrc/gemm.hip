@@ -137,12 +137,18 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
   const uint8_t* sb0 = sm0 + (size_t)e * ((size_t)N * K / 16);
   const uint8_t* qb1 = GATEUP ? qm1 + (size_t)e * ((size_t)N * K / 2) : qb0;
   const uint8_t* sb1 = GATEUP ? sm1 + (size_t)e * ((size_t)N * K / 16) : sb0;
+  // The lane loads weight row pr of its 32-row tile rather than row r32, chosen so that, with
+  // the weights as the first MFMA operand, accumulator element v of lane l is feature
+  // 16 (l / 32) + v of the tile: each lane then holds 16 consecutive features of one token row
+  // (pr has the parity of r32, so the scale byte sits in the same half of its dword).
+  const int pr = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
   uint32_t qoff[2], soff[2];
   int feat[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = GATEUP ? fb * (32 * NW) + wn * 32 + r32 : fb * (64 * NW) + wn * 64 + t * 32 + r32;
-    feat[t] = row;
+    const int row0 = GATEUP ? fb * (32 * NW) + wn * 32 : fb * (64 * NW) + wn * 64 + t * 32;
+    const int row = row0 + pr;
+    feat[t] = row0;  // first feature of the tile
     const int rc = min(row, N - 1);
     const uint32_t tile0 = (uint32_t)(rc >> 4) * (uint32_t)nchunk;
     qoff[t] = tile0 * 1024u + (uint32_t)(rc & 15) * 16u + (uint32_t)hgrp * 256u;
@@ -241,29 +247,26 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     }
   }
 
-  // epilogue.  With the weights as the first operand, element v of lane l of a 32x32
-  // accumulator is row (token) l % 32 of the sub-tile and feature (v / 4) * 8 + (l / 32) * 4 +
-  // v % 4 of the weight tile: every lane holds four runs of four consecutive features of one
-  // row, stored as 8-byte (f16) or 16-byte (fp32) vectors.
+  // epilogue.  With the weights as the first operand and the row order above, lane l holds
+  // features 16 (l / 32) .. + 15 of its weight tile for token row l % 32 of each 32-row
+  // sub-tile: two 16-byte (f16) or four 16-byte (fp32) stores per row and tile.
   if (GATEUP) {
     const float tsg = ts[e * 3 + 0], tsu = ts[e * 3 + 1];
     _Float16* h16 = reinterpret_cast<_Float16*>(out);
-    const int f0 = feat[0] - r32;  // first feature of the gate tile (= of the up tile)
+    const int f0 = feat[0];  // first feature of the gate tile (= of the up tile)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = m0 + i * 32 + r32;
       if (m < rows && f0 < I) {
-        _Float16* dst = h16 + (size_t)(base + m) * I + f0 + hgrp * 4;
+        f16x8 o[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f16x4 o;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float gv = acc[i][0][4 * g4 + c] * tsg, uv = acc[i][1][4 * g4 + c] * tsu;
-            o[c] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
-          }
-          *reinterpret_cast<f16x4*>(dst + 8 * g4) = o;
+        for (int v = 0; v < 16; ++v) {
+          const float gv = acc[i][0][v] * tsg, uv = acc[i][1][v] * tsu;
+          o[v >> 3][v & 7] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
         }
+        f16x8* dst = reinterpret_cast<f16x8*>(h16 + (size_t)(base + m) * I + f0 + hgrp * 16);
+        dst[0] = o[0];
+        dst[1] = o[1];
       }
     }
   } else {
@@ -274,21 +277,22 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
       if (m >= rows) continue;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int f0 = feat[t] - r32;
+        const int f0 = feat[t];
         if (f0 >= N) continue;  // N is a multiple of 32: a tile is wholly in or out
-        const size_t o = (size_t)(base + m) * H + f0 + hgrp * 4;
+        const size_t o = (size_t)(base + m) * H + f0 + hgrp * 16;
+        if (Y_F16) {
+          f16x8 v8[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          if (Y_F16) {
-            const f16x4 v = {(_Float16)(acc[i][t][4 * g4] * tsd), (_Float16)(acc[i][t][4 * g4 + 1] * tsd),
-                             (_Float16)(acc[i][t][4 * g4 + 2] * tsd),
-                             (_Float16)(acc[i][t][4 * g4 + 3] * tsd)};
-            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(out) + o + 8 * g4) = v;
-          } else {
-            const f32x4 v = {acc[i][t][4 * g4] * tsd, acc[i][t][4 * g4 + 1] * tsd,
-                             acc[i][t][4 * g4 + 2] * tsd, acc[i][t][4 * g4 + 3] * tsd};
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o + 8 * g4) = v;
-          }
+          for (int v = 0; v < 16; ++v) v8[v >> 3][v & 7] = (_Float16)(acc[i][t][v] * tsd);
+          f16x8* dst = reinterpret_cast<f16x8*>(reinterpret_cast<_Float16*>(out) + o);
+          dst[0] = v8[0];
+          dst[1] = v8[1];
+        } else {
+          f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[q] = f32x4{acc[i][t][4 * q] * tsd, acc[i][t][4 * q + 1] * tsd,
+                           acc[i][t][4 * q + 2] * tsd, acc[i][t][4 * q + 3] * tsd};
         }
       }
     }

@@ -234,7 +234,12 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     soff = srs * (uint32_t)(K / 32);
   }
 
-  // this wavefront's two weight tiles (32-row tile indices, clamped to the matrix)
+  // this wavefront's two weight tiles (32-row tile indices, clamped to the matrix).  The lane
+  // reads the operand bytes and scale dword of row pr of the tile (lane slot pr + 32 hh) rather
+  // than row r32, so that, with the weights as the first MFMA operand, accumulator element v of
+  // lane l is feature 16 (l / 32) + v of the tile: 16 consecutive features of one token row.
+  const int pr = ((r32 >> 2) & 1) * 16 + (r32 >> 3) * 4 + (r32 & 3);
+  const int slot = pr + 32 * hh;
   int feat[2];
   const uint8_t* qt[2];
   const uint8_t* stl[2];
@@ -246,8 +251,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     const size_t tix = (size_t)e * (N / 32) + tile;
     const uint8_t* qm = GATEUP && t == 1 ? q1 : q0;
     const uint8_t* sm = GATEUP && t == 1 ? s1 : s0;
-    qt[t] = qm + tix * (size_t)nst * 2048 + lane * 32;
-    stl[t] = sm + tix * (size_t)(nst / 4) * 256 + lane * 4;
+    qt[t] = qm + tix * (size_t)nst * 2048 + slot * 32;
+    stl[t] = sm + tix * (size_t)(nst / 4) * 256 + slot * 4;
   }
 
   struct Stage {
@@ -333,10 +338,9 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
     st += 4;
   } while (st < nst);
 
-  // epilogue.  The weights are the first operand, so each 32x32 accumulator is the transposed
-  // tile: element v of lane l is row (token) l % 32 of the sub-tile and feature
-  // (v / 4) * 8 + (l / 32) * 4 + v % 4 of the weight tile, i.e. every lane holds four runs of
-  // four consecutive features of one row.
+  // epilogue.  The weights are the first operand and their rows are read in the order above:
+  // lane l holds features 16 (l / 32) .. + 15 of its weight tile for token row l % 32 of each
+  // 32-row sub-tile.
   if (GATEUP) {
     uint8_t* h8 = reinterpret_cast<uint8_t*>(out);
     const int f0 = feat[0];  // the gate tile and the up tile hold the same 32 features
@@ -354,15 +358,14 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
       amax = fmaxf(amax, __shfl_xor(amax, 32));
       const int E = mx8_exp(amax);
       if (m < rows && f0 < N) {
-        uint8_t* dst = h8 + (size_t)(base + m) * I + f0 + hh * 4;
+        uint32_t w[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const uint32_t w = amax > 0.f ? e4m3_pack4(ldexpf(hv[4 * g4], -E), ldexpf(hv[4 * g4 + 1], -E),
-                                                     ldexpf(hv[4 * g4 + 2], -E),
-                                                     ldexpf(hv[4 * g4 + 3], -E))
-                                        : 0u;
-          *reinterpret_cast<uint32_t*>(dst + 8 * g4) = w;
-        }
+        for (int g4 = 0; g4 < 4; ++g4)
+          w[g4] = amax > 0.f ? e4m3_pack4(ldexpf(hv[4 * g4], -E), ldexpf(hv[4 * g4 + 1], -E),
+                                          ldexpf(hv[4 * g4 + 2], -E), ldexpf(hv[4 * g4 + 3], -E))
+                             : 0u;
+        *reinterpret_cast<uint4*>(h8 + (size_t)(base + m) * I + f0 + hh * 16) =
+            make_uint4(w[0], w[1], w[2], w[3]);
         if (hh == 0) hs_out[(size_t)(base + m) * (I / 32) + f0 / 32] = (uint8_t)(E + 127);
       }
     }
@@ -376,13 +379,12 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
       for (int t = 0; t < 2; ++t) {
         const int f0 = feat[t];
         if (f0 >= N) continue;  // N is a multiple of 32: a tile is wholly in or out
-        _Float16* dst = y + (size_t)(base + m) * H + f0 + hh * 4;
+        f16x8 o[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f16x4 o = {(_Float16)acc[i][t][4 * g4], (_Float16)acc[i][t][4 * g4 + 1],
-                           (_Float16)acc[i][t][4 * g4 + 2], (_Float16)acc[i][t][4 * g4 + 3]};
-          *reinterpret_cast<f16x4*>(dst + 8 * g4) = o;
-        }
+        for (int v = 0; v < 16; ++v) o[v >> 3][v & 7] = (_Float16)acc[i][t][v];
+        f16x8* dst = reinterpret_cast<f16x8*>(y + (size_t)(base + m) * H + f0 + hh * 16);
+        dst[0] = o[0];
+        dst[1] = o[1];
       }
     }
   }
