@@ -73,8 +73,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
 #pragma unroll
     for (int u = 0; u < kSet; ++u) {
       const int c = min(c0 + u, nchunk - 1);  // clamped: past the end re-reads the last chunk
-      qg[u] = *reinterpret_cast<const uint4*>(gqp + c * 1024);
-      qu[u] = *reinterpret_cast<const uint4*>(uqp + c * 1024);
+      qg[u] = load_stream16(gqp + c * 1024);
+      qu[u] = load_stream16(uqp + c * 1024);
       sg[u] = load_u16(gsp + c * 128);
       su[u] = load_u16(usp + c * 128);
     }
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
 #pragma unroll
     for (int u = 0; u < kSet; ++u) {
       const int c = min(c0 + u, nchunk - 1);
-      q[u] = *reinterpret_cast<const uint4*>(qp + c * 1024);
+      q[u] = load_stream16(qp + c * 1024);
       sc[u] = load_u16(sp + c * 128);
     }
   };

@@ -254,8 +254,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
 #pragma unroll
     for (int u = 0; u < kLsSetC; ++u) {
       const int ch = min(cs + u, nch - 1);
-      qg[u] = *reinterpret_cast<const uint4*>(a.gq + tq + (size_t)ch * 1024);
-      qu[u] = *reinterpret_cast<const uint4*>(a.uq + tq + (size_t)ch * 1024);
+      qg[u] = load_stream16(a.gq + tq + (size_t)ch * 1024);
+      qu[u] = load_stream16(a.uq + tq + (size_t)ch * 1024);
       sg[u] = load_u16(a.gs + ts_ + (size_t)ch * 128);
       su[u] = load_u16(a.us + ts_ + (size_t)ch * 128);
     }
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
 #pragma unroll
       for (int u = 0; u < kLsSetD; ++u) {
         const int c = min(cs + u, nck - 1);
-        q[u] = *reinterpret_cast<const uint4*>(a.dq + tq + (size_t)c * 1024);
+        q[u] = load_stream16(a.dq + tq + (size_t)c * 1024);
         sc[u] = load_u16(a.ds + ts_ + (size_t)c * 128);
       }
     };
