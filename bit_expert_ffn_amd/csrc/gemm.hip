@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     ffn_plan(count, offset, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
-// Block: NW wavefronts side by side in N; MT = 64 * WM rows x 64 NW weight rows; K in stages of
+// Block: NW wavefronts side by side in N; MT rows x 64 NW weight rows; K in stages of
 // 64.  Every wavefront computes all MT rows (MI = MT / 32 tiles of 32) against its own 2 weight
 // tiles of 32 rows:
 //   gate/up: wavefront wn takes features f0 + 32 wn .. + 31 of the block's 32 NW: its gate tile
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
 // K may be permuted: step i takes codes 8i..8i+7 of the lane's group, and the activation
 // operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
 // loads of activations and packed weights run ahead in S register sets.
-template <bool GATEUP, int WM, bool Y_F16, int S, int NW>
+template <bool GATEUP, int MTT, bool Y_F16, int S, int NW>
 __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     const int32_t* __restrict__ sorted_slot, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int k, int H, int I, void* __restrict__ out) {
   constexpr int NTH = 64 * NW;      // threads per block
-  constexpr int MT = 64 * WM;
+  constexpr int MT = MTT;
   constexpr int MI = MT / 32;        // 32-row tiles per wavefront
   constexpr int NA = MT * 8 / NTH;   // 16-byte activation pieces per thread per stage
   static_assert(NA >= 1, "block tile too small for its threads");
@@ -299,7 +299,8 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
   }
 }
 
-int gemm_rows_per_tile(int T) { return T >= 2048 ? 128 : 64; }
+// rows of a grouped-GEMM tile (the f16 path)
+int gemm_rows_per_tile(int T) { return T >= 2048 ? 128 : T >= 512 ? 64 : 32; }
 
 size_t gemm_max_tiles(int T, int k, int E) {
   const int MT = gemm_rows_per_tile(T);
@@ -316,11 +317,13 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
   x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
       a.x, a.x16, n8, a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles, max_tiles,
       n_tiles);
-  // 128-row tiles: 8 wavefronts (512 weight rows per block); 64-row tiles (fewer rows, fewer
-  // blocks): 4 wavefronts
+  // 128-row tiles from 2048 tokens: 8 wavefronts (512 weight rows per block); 64-row tiles from
+  // 512 tokens and 32-row tiles below, on 4 wavefronts: most experts of a small batch have a
+  // few rows, and a smaller tile wastes fewer matrix-core cycles on rows past the expert's end
+  // (measured at T = 128: 130 against 153 us; at T = 64: 954 against 965 us)
 #define MOE_GEMM(GU_, WM_, F16_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
   do {                                                                                        \
-    constexpr int NW_ = WM_ == 2 ? 8 : 4;                                                     \
+    constexpr int NW_ = WM_ == 128 ? 8 : 4;                                                   \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
     ffn_gemm_kernel<GU_, WM_, F16_, kGemmSets, NW_><<<g_, 64 * NW_, 0, s>>>(                  \
@@ -328,13 +331,17 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
         a.H, a.I, OUT_);                                                                      \
   } while (0)
   if (MT == 128) {
-    MOE_GEMM(true, 2, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 2, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 2, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    MOE_GEMM(true, 128, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16) MOE_GEMM(false, 128, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else MOE_GEMM(false, 128, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+  } else if (MT == 64) {
+    MOE_GEMM(true, 64, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16) MOE_GEMM(false, 64, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else MOE_GEMM(false, 64, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
   } else {
-    MOE_GEMM(true, 1, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 1, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 1, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    MOE_GEMM(true, 32, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16) MOE_GEMM(false, 32, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else MOE_GEMM(false, 32, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
   }
 #undef MOE_GEMM
   return hipGetLastError();

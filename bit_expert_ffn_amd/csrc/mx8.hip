@@ -391,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void mx8_gemm_kernel(
 }
 
 hipError_t launch_ffn_mx8(const Mx8Args& a, hipStream_t s) {
-  const int MT = gemm_rows_per_tile(a.T);
+  const int MT = a.T >= 2048 ? 128 : 64;  // the kernel's tiles: 128 or 64 rows (max_tiles bounds both)
   const int max_tiles = (int)gemm_max_tiles(a.T, a.k, a.E);
   const size_t nblk = (size_t)a.T * a.H / 32;
   x_to_mx8_plan_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, s>>>(

@@ -24,6 +24,8 @@ SHAPES = {
     "one_token": dict(T=1, H=1024, I=256, E=32, k=8, router="normal", zipf=None),
     "two_tokens": dict(T=2, H=512, I=384, E=16, k=4, router="normal", zipf=None),
     "one_token_wide": dict(T=1, H=7168, I=256, E=8, k=2, router="normal", zipf=None),
+    # 512 <= T < 2048: 64-row GEMM tiles (32-row below, 128-row from 2048)
+    "mid_64_row_tiles": dict(T=600, H=256, I=256, E=16, k=4, router="normal", zipf=None),
 }
 
 
