@@ -9,7 +9,7 @@
 //
 // Dispatch: every expert has at most T rows (a token's k experts are distinct).  The host picks
 // R in {0, 1, 2, 4} from T; experts with <= R rows run the VALU kernels below, the others the
-// matrix-core grouped GEMM (gemm.hip); from 128 tokens up R = 0 and the GEMM takes every expert.  Both read the tile-major weight layout (pack.hip): for a
+// matrix-core grouped GEMM (gemm.hip); from 32 tokens up R = 0 and the GEMM takes every expert.  Both read the tile-major weight layout (pack.hip): for a
 // 16-feature row tile and a 128-column chunk, lane l = 16*g + n of a wavefront loads feature
 // n's 32 values K = [c*128 + g*32, +32) (16 bytes) and their two e4m3 scale bytes; the
 // wavefront's 64 loads are one contiguous 1 KB block.
@@ -273,12 +273,12 @@ static int few_ksplit(int tiles, int nchunk) {
   return ks;
 }
 
-// Largest row count of a "few-row" expert; 0 sends every expert to the grouped GEMM.  From 128
-// tokens up the grouped GEMM streams the experts faster than the VALU kernels (measured at
-// T = 128, I = 256: 165 against 190 us), below it the VALU kernels win (T = 64, I = 2048: 1050
-// against 1206 us).
+// Largest row count of a "few-row" expert; 0 sends every expert to the grouped GEMM.  From 32
+// tokens up the grouped GEMM (32-row tiles, streamed weight loads) is faster than the VALU
+// kernels (measured at T = 64, I = 2048: expert FFN 915 against 978 us; at T = 128, I = 256:
+// 130 against 190 us).
 static int few_rows(int T, int H, int I) {
-  int R = T <= 1 ? 1 : T <= 2 ? 2 : T < 128 ? 4 : 0;
+  int R = T <= 1 ? 1 : T <= 2 ? 2 : T < 32 ? 4 : 0;
   const int kmax = H > I ? H : I;
   while (R > 0 && (size_t)R * kmax * 2 > 65536) R >>= 1;
   return R;

@@ -170,8 +170,15 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     // g = 2 (st % 2) + lane / 32 (the lane / 32 part is already in qoff / soff)
     const uint32_t cq = (uint32_t)(st >> 1) * 1024u + (uint32_t)(st & 1) * 512u;
     const uint32_t cs = (uint32_t)(st >> 1) * 128u + (uint32_t)(st & 1) * 64u;
-    r.q0 = *reinterpret_cast<const u32x4*>(qb0 + (qoff[0] + cq));
-    r.q1 = *reinterpret_cast<const u32x4*>(qbt1 + (qoff[1] + cq));
+    // 32-row tiles (small batches): an expert has one or two tiles, so its weights are read
+    // about once: non-temporal loads.  Larger tiles share weight slices through L2.
+    if (MT == 32) {
+      r.q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qb0 + (qoff[0] + cq)));
+      r.q1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qbt1 + (qoff[1] + cq)));
+    } else {
+      r.q0 = *reinterpret_cast<const u32x4*>(qb0 + (qoff[0] + cq));
+      r.q1 = *reinterpret_cast<const u32x4*>(qbt1 + (qoff[1] + cq));
+    }
     // the lane's two scale bytes sit in the low (even row) or high (odd row) half of an aligned
     // dword; loading the whole dword keeps the value free of any zero-extension, which the
     // compiler would otherwise place right after the load (in the previous step) and so wait
