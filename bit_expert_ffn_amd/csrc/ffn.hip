@@ -284,7 +284,7 @@ static int few_rows(int T, int H, int I) {
   return R;
 }
 
-// A second stream per device for the busy experts' chain (x -> f16 + plan, grouped GEMMs).  It
+// A second stream per device for the busy experts' chain (tile plan, grouped GEMMs).  It
 // shares no data with the few-row chain (disjoint experts, so disjoint rows of h and y, and its
 // own workspace regions), so the two run side by side and the caller's stream waits for both.
 // Created once per device with the default priority; work of calls from several threads

@@ -7,12 +7,13 @@
 // 4-bit weights unpacked on chip and never written back dequantised ("Optimizing Models to Be
 // Fast at Codegen", section 2).
 //
-// Work list: ffn_plan (run by the first block of the activation-conversion kernel) walks the
+// Work list: ffn_plan (a one-wavefront kernel launched before the GEMMs) walks the
 // active experts in order and lists every tile of MT rows of every expert with at least
 // min_rows rows, each with its expert's descriptor (expert, first tile, rows, first row).  grid.y runs over a host-side bound of that list; blocks
 // past its end return.  Nothing is read back by the host.
 //
-// Arithmetic: activations (x or h) and decoded weights enter v_mfma_f32_32x32x16_f16 as f16;
+// Arithmetic: activations (x, converted from bf16 on its way into LDS, or h) and decoded weights
+// enter v_mfma_f32_32x32x16_f16 as f16;
 // e2m1 * e4m3 is exact in f16 (at most 6 significant bits, magnitude in [2^-10, 2688]); the
 // fp32 tensor scales multiply the fp32 accumulators in the epilogue.
 #include "common.h"
@@ -32,8 +33,8 @@ __device__ inline f16x8 gdecode8(uint32_t q, f16x2 s) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// x [T][H] bf16 -> f16 (8 values per thread); block 0's first wavefront also builds the tile
-// list of the busy experts.
+// x [T][H] bf16 -> f16 (8 values per thread, for 128-row tiles); block 0's first wavefront also
+// builds the tile list of the busy experts.
 __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     const uint16_t* __restrict__ x, _Float16* __restrict__ x16, size_t n8,
     const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
@@ -55,6 +56,14 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
     ffn_plan(count, offset, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
+// The tile list of the busy experts alone (one wavefront; smaller tiles, whose GEMM converts x).
+__global__ __launch_bounds__(64) void ffn_plan_kernel(
+    const int32_t* __restrict__ count, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int MT,
+    int min_rows, int4* __restrict__ tiles, int max_tiles, int32_t* __restrict__ n_tiles) {
+  ffn_plan(count, offset, active, n_active, MT, min_rows, tiles, max_tiles, n_tiles);
+}
+
 // Block: NW wavefronts side by side in N; MT rows x 64 NW weight rows; K in stages of
 // 64.  Every wavefront computes all MT rows (MI = MT / 32 tiles of 32) against its own 2 weight
 // tiles of 32 rows:
@@ -71,9 +80,9 @@ __global__ __launch_bounds__(256) void x_to_f16_plan_kernel(
 // K may be permuted: step i takes codes 8i..8i+7 of the lane's group, and the activation
 // operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
 // loads of activations and packed weights run ahead in S register sets.
-template <bool GATEUP, int MTT, bool Y_F16, int S, int NW>
+template <bool GATEUP, int MTT, bool Y_F16, int S, int NW, bool XBF>
 __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
-    const _Float16* __restrict__ xa, const uint8_t* __restrict__ qm0,
+    const uint16_t* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
     const int32_t* __restrict__ sorted_slot, const int4* __restrict__ tiles,
@@ -187,11 +196,25 @@ __global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
     r.s1 = *reinterpret_cast<const uint32_t*>(sbt1 + ((soff[1] + cs) & ~3u));
   };
   auto store_a = [&](const Stage& r, int buf) __attribute__((always_inline)) {
-    // piece i of this thread: s = tid + NTH * i -> row s >> 3, 16-byte column s & 7
+    // piece i of this thread: s = tid + NTH * i -> row s >> 3, 16-byte column s & 7.  With XBF
+    // (gate/up on 32- and 64-row tiles) the activations are bf16 x, converted here (round to
+    // nearest even, as a bf16 -> f16 cast does); 128-row tiles read x converted once by
+    // x_to_f16_plan_kernel, since every weight block of a tile would otherwise convert it again
     const int c8 = (tid & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + (NTH / 8) * i][c8]) = r.a[i];
+    for (int i = 0; i < NA; ++i) {
+      u32x4 v = r.a[i];
+      if (XBF) {
+        f16x8 hv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hv[2 * j] = (_Float16)__uint_as_float(v[j] << 16);
+          hv[2 * j + 1] = (_Float16)__uint_as_float(v[j] & 0xffff0000u);
+        }
+        v = __builtin_bit_cast(u32x4, hv);
+      }
+      *reinterpret_cast<u32x4*>(&As[buf][(tid >> 3) + (NTH / 8) * i][c8]) = v;
+    }
   };
 
   f32x16 acc[MI][2];
@@ -320,36 +343,44 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
                            hipStream_t s) {
   const int MT = gemm_rows_per_tile(a.T);
   const int max_tiles = (int)gemm_max_tiles(a.T, a.k, a.E);
-  const size_t n8 = (size_t)a.T * a.H / 8;
-  x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
-      a.x, a.x16, n8, a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles, max_tiles,
-      n_tiles);
+  if (MT == 128) {
+    const size_t n8 = (size_t)a.T * a.H / 8;
+    x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
+        a.x, a.x16, n8, a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles, max_tiles,
+        n_tiles);
+  } else {
+    ffn_plan_kernel<<<1, 64, 0, s>>>(a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles,
+                                     max_tiles, n_tiles);
+  }
   // 128-row tiles from 2048 tokens: 8 wavefronts (512 weight rows per block); 64-row tiles from
   // 512 tokens and 32-row tiles below, on 4 wavefronts: most experts of a small batch have a
   // few rows, and a smaller tile wastes fewer matrix-core cycles on rows past the expert's end
   // (measured at T = 128: 130 against 153 us; at T = 64: 954 against 965 us)
-#define MOE_GEMM(GU_, WM_, F16_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                         \
+#define MOE_GEMM(GU_, MT_, F16_, XBF_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                           \
   do {                                                                                        \
-    constexpr int NW_ = WM_ == 128 ? 8 : 4;                                                   \
+    constexpr int NW_ = MT_ == 128 ? 8 : 4;                                                   \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
-    ffn_gemm_kernel<GU_, WM_, F16_, kGemmSets, NW_><<<g_, 64 * NW_, 0, s>>>(                  \
-        XA_, Q0_, S0_, Q1_, S1_, a.ts, a.sorted_slot, tiles, n_tiles, a.k,                     \
+    ffn_gemm_kernel<GU_, MT_, F16_, kGemmSets, NW_, XBF_><<<g_, 64 * NW_, 0, s>>>(            \
+        (const uint16_t*)(XA_), Q0_, S0_, Q1_, S1_, a.ts, a.sorted_slot, tiles, n_tiles, a.k,  \
         a.H, a.I, OUT_);                                                                      \
   } while (0)
-  if (MT == 128) {
-    MOE_GEMM(true, 128, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 128, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 128, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-  } else if (MT == 64) {
-    MOE_GEMM(true, 64, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 64, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 64, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-  } else {
-    MOE_GEMM(true, 32, false, a.x16, a.gq, a.gs, a.uq, a.us, a.h16);
-    if (a.y_f16) MOE_GEMM(false, 32, true, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-    else MOE_GEMM(false, 32, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
-  }
+#define MOE_GEMM_MT(MT_, XBF_)                                                                 \
+  do {                                                                                        \
+    MOE_GEMM(true, MT_, false, XBF_, XBF_ ? (const void*)a.x : (const void*)a.x16, a.gq, a.gs, \
+             a.uq, a.us, a.h16);                                                              \
+    if (a.y_f16)                                                                              \
+      MOE_GEMM(false, MT_, true, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);                  \
+    else                                                                                      \
+      MOE_GEMM(false, MT_, false, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);                 \
+  } while (0)
+  if (MT == 128)
+    MOE_GEMM_MT(128, false);
+  else if (MT == 64)
+    MOE_GEMM_MT(64, true);
+  else
+    MOE_GEMM_MT(32, true);
+#undef MOE_GEMM_MT
 #undef MOE_GEMM
   return hipGetLastError();
 }
