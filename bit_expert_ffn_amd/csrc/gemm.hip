@@ -356,30 +356,36 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
   // 512 tokens and 32-row tiles below, on 4 wavefronts: most experts of a small batch have a
   // few rows, and a smaller tile wastes fewer matrix-core cycles on rows past the expert's end
   // (measured at T = 128: 130 against 153 us; at T = 64: 954 against 965 us)
-#define MOE_GEMM(GU_, MT_, F16_, XBF_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                           \
+#define MOE_GEMM(GU_, MT_, S_, F16_, XBF_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                       \
   do {                                                                                        \
     constexpr int NW_ = MT_ == 128 ? 8 : 4;                                                   \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
-    ffn_gemm_kernel<GU_, MT_, F16_, kGemmSets, NW_, XBF_><<<g_, 64 * NW_, 0, s>>>(            \
+    ffn_gemm_kernel<GU_, MT_, F16_, S_, NW_, XBF_><<<g_, 64 * NW_, 0, s>>>(                   \
         (const uint16_t*)(XA_), Q0_, S0_, Q1_, S1_, a.ts, a.sorted_slot, tiles, n_tiles, a.k,  \
         a.H, a.I, OUT_);                                                                      \
   } while (0)
-#define MOE_GEMM_MT(MT_, XBF_)                                                                 \
+#define MOE_GEMM_MT(MT_, S_, XBF_)                                                             \
   do {                                                                                        \
-    MOE_GEMM(true, MT_, false, XBF_, XBF_ ? (const void*)a.x : (const void*)a.x16, a.gq, a.gs, \
-             a.uq, a.us, a.h16);                                                              \
+    MOE_GEMM(true, MT_, S_, false, XBF_, XBF_ ? (const void*)a.x : (const void*)a.x16, a.gq,   \
+             a.gs, a.uq, a.us, a.h16);                                                        \
     if (a.y_f16)                                                                              \
-      MOE_GEMM(false, MT_, true, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);                  \
+      MOE_GEMM(false, MT_, S_, true, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);              \
     else                                                                                      \
-      MOE_GEMM(false, MT_, false, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);                 \
+      MOE_GEMM(false, MT_, S_, false, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);             \
   } while (0)
+  // register sets of the load pipeline: 4, or 6 for a small batch of narrow experts (I <= 512),
+  // whose few blocks are each bound by the bytes they keep in flight (measured at T = 128,
+  // I = 256: 122 against 132 us; at T = 64, I = 2048, where the blocks fill the chip, 6 sets
+  // cost occupancy: 943 against 921 us)
   if (MT == 128)
-    MOE_GEMM_MT(128, false);
+    MOE_GEMM_MT(128, kGemmSets, false);
   else if (MT == 64)
-    MOE_GEMM_MT(64, true);
+    MOE_GEMM_MT(64, kGemmSets, true);
+  else if (a.I <= 512)
+    MOE_GEMM_MT(32, 6, true);
   else
-    MOE_GEMM_MT(32, true);
+    MOE_GEMM_MT(32, kGemmSets, true);
 #undef MOE_GEMM_MT
 #undef MOE_GEMM
   return hipGetLastError();
