@@ -106,10 +106,12 @@ MOE_API moe_status moe_route(const void* x_dev, const float* w_router_dev, const
                                     (hipStream_t)stream));
 }
 
-MOE_API moe_status moe_group(const int32_t* topk_id_dev, int32_t T, int32_t k, int32_t E,
-                             int32_t* count_dev, int32_t* offset_dev, int32_t* sorted_slot_dev,
-                             int32_t* slot_row_dev, int32_t* active_dev, int32_t* n_active_dev,
-                             void* ws_dev, size_t ws_bytes, void* stream) {
+// moe_group; with plan, the grouping kernel also writes the busy experts' tile list
+static moe_status group_run(const int32_t* topk_id_dev, int32_t T, int32_t k, int32_t E,
+                            int32_t* count_dev, int32_t* offset_dev, int32_t* sorted_slot_dev,
+                            int32_t* slot_row_dev, int32_t* active_dev, int32_t* n_active_dev,
+                            void* ws_dev, size_t ws_bytes, void* stream,
+                            const moe::GroupPlan* plan) {
   if (!topk_id_dev || !count_dev || !offset_dev || !sorted_slot_dev || !slot_row_dev ||
       !active_dev || !n_active_dev)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -127,15 +129,24 @@ MOE_API moe_status moe_group(const int32_t* topk_id_dev, int32_t T, int32_t k, i
   int32_t* whist = reinterpret_cast<int32_t*>((char*)ws_dev + L.group_whist);
   return from_hip(moe::launch_group(topk_id_dev, T, k, E, count_dev, offset_dev,
                                     sorted_slot_dev, slot_row_dev, active_dev, n_active_dev,
-                                    whist, (hipStream_t)stream));
+                                    whist, (hipStream_t)stream, plan));
 }
 
-MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_experts* w,
-                                        const int32_t* count_dev, const int32_t* offset_dev,
-                                        const int32_t* sorted_slot_dev, const int32_t* active_dev,
-                                        const int32_t* n_active_dev, int32_t T, int32_t k,
-                                        void* y_dev, int32_t y_dtype, void* ws_dev,
-                                        size_t ws_bytes, void* stream) {
+MOE_API moe_status moe_group(const int32_t* topk_id_dev, int32_t T, int32_t k, int32_t E,
+                             int32_t* count_dev, int32_t* offset_dev, int32_t* sorted_slot_dev,
+                             int32_t* slot_row_dev, int32_t* active_dev, int32_t* n_active_dev,
+                             void* ws_dev, size_t ws_bytes, void* stream) {
+  return group_run(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
+                   active_dev, n_active_dev, ws_dev, ws_bytes, stream, nullptr);
+}
+
+// moe_expert_ffn_nvfp4; planned: the tile list in the workspace is already written
+static moe_status expert_ffn_run(const void* x_dev, const moe_nvfp4_experts* w,
+                                 const int32_t* count_dev, const int32_t* offset_dev,
+                                 const int32_t* sorted_slot_dev, const int32_t* active_dev,
+                                 const int32_t* n_active_dev, int32_t T, int32_t k, void* y_dev,
+                                 int32_t y_dtype, void* ws_dev, size_t ws_bytes, void* stream,
+                                 int planned) {
   if (!x_dev || !w || !count_dev || !offset_dev || !sorted_slot_dev || !active_dev ||
       !n_active_dev || !y_dev || !ws_dev)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -164,9 +175,20 @@ MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_exper
   a.y_f16 = y_dtype == MOE_F16;
   a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
   a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
+  a.planned = planned;
   int4* tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn(a, tiles, n_tiles, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_experts* w,
+                                        const int32_t* count_dev, const int32_t* offset_dev,
+                                        const int32_t* sorted_slot_dev, const int32_t* active_dev,
+                                        const int32_t* n_active_dev, int32_t T, int32_t k,
+                                        void* y_dev, int32_t y_dtype, void* ws_dev,
+                                        size_t ws_bytes, void* stream) {
+  return expert_ffn_run(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
+                        n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream, 0);
 }
 
 MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t* slot_row_dev,
@@ -266,11 +288,22 @@ MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
   st = moe_route(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_id_dev, topk_w_dev,
                  ws_dev, ws_bytes, stream);
   if (st != MOE_OK) return st;
-  st = moe_group(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
-                 active_dev, n_active_dev, ws_dev, ws_bytes, stream);
+  // the one-block grouping also writes the busy experts' tile list, which saves the FFN call's
+  // one-wavefront planning launch
+  moe::GroupPlan gp{0, 0, 0, nullptr, nullptr};
+  const bool fuse = (size_t)T * k <= (size_t)moe::kGroupSmallMax &&
+                    moe::ffn_separate_plan(T, H, I, &gp.MT, &gp.min_rows);
+  if (fuse) {
+    gp.max_tiles = (int)moe::gemm_max_tiles(T, k, E);
+    gp.tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
+    gp.n_tiles = reinterpret_cast<int32_t*>(gp.tiles + gp.max_tiles);
+  }
+  st = group_run(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
+                 active_dev, n_active_dev, ws_dev, ws_bytes, stream, fuse ? &gp : nullptr);
   if (st != MOE_OK) return st;
-  st = moe_expert_ffn_nvfp4(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
-                            n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream);
+  st = expert_ffn_run(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
+                      n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream,
+                      fuse ? 1 : 0);
   if (st != MOE_OK) return st;
   return moe_combine(y_dev, y_dtype, slot_row_dev, topk_w_dev, T, k, H, out_dev, stream);
 }

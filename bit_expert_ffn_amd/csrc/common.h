@@ -61,9 +61,17 @@ WsLayout ws_layout(int T, int H, int I, int E, int k);
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                         int E, int k, float* logits, int32_t* topk_id, float* topk_w,
                         float* partial, uint16_t* wsplit, hipStream_t s);
+// plan_MT > 0 (one-block grouping only, T * k <= kGroupSmallMax): the grouping kernel also
+// writes the busy experts' tile list, as ffn_plan would.
+struct GroupPlan {
+  int MT, min_rows, max_tiles;
+  int4* tiles;
+  int32_t* n_tiles;
+};
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* count,
                         int32_t* offset, int32_t* sorted_slot, int32_t* slot_row,
-                        int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s);
+                        int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s,
+                        const GroupPlan* plan = nullptr);
 
 struct FfnArgs {
   const uint16_t* x;  // [T][H] bf16
@@ -75,11 +83,16 @@ struct FfnArgs {
   int y_f16;
   _Float16* x16;  // workspace
   _Float16* h16;  // workspace
+  int planned;    // the tile list of the busy experts is already written (by the grouping)
 };
 hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream_t s);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t* n_tiles,
                            hipStream_t s);
 int gemm_rows_per_tile(int T);
+// Tile list that the expert-FFN call writes in a one-wavefront kernel of its own: false if it
+// writes none there (no expert can be busy, or 128-row tiles, whose list comes with the x
+// conversion); else its rows per tile and the fewest rows of a listed expert.
+bool ffn_separate_plan(int T, int H, int I, int* MT, int* min_rows);
 size_t gemm_max_tiles(int T, int k, int E);
 
 // fp8 variant of the expert FFN (mx8.hip): MXFP8 weights in the tile layout of the scaled
@@ -145,15 +158,13 @@ hipError_t launch_combine_norm(const CombineNormArgs& a, int y_f16, hipStream_t 
 // List the MT-row tiles of every expert with >= min_rows rows (one wavefront).  Every tile
 // of expert e gets the same descriptor {e, index of e's first tile, rows of e, first grouped
 // row of e}: a tile's own first row is (its index - the first index) * MT, and the expert's
-// tiles are consecutive in the list.
-__device__ inline void ffn_plan(const int32_t* __restrict__ count,
-                                const int32_t* __restrict__ offset,
-                                const int32_t* __restrict__ active,
-                                const int32_t* __restrict__ n_active, int MT, int min_rows,
-                                int4* __restrict__ tiles, int max_tiles,
-                                int32_t* __restrict__ n_tiles) {
+// tiles are consecutive in the list.  count, offset and active may be in global memory or in
+// LDS (generic pointers); na is the number of active experts.
+__device__ inline void ffn_plan_n(const int32_t* count, const int32_t* offset,
+                                  const int32_t* active, int na, int MT, int min_rows,
+                                  int4* __restrict__ tiles, int max_tiles,
+                                  int32_t* __restrict__ n_tiles) {
   const int lane = threadIdx.x & 63;
-  const int na = *n_active;
   int ex[4], nt[4], cnt[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -179,6 +190,14 @@ __device__ inline void ffn_plan(const int32_t* __restrict__ count,
     start += nt[i];
   }
   if (lane == 63) *n_tiles = incl < max_tiles ? incl : max_tiles;
+}
+__device__ inline void ffn_plan(const int32_t* __restrict__ count,
+                                const int32_t* __restrict__ offset,
+                                const int32_t* __restrict__ active,
+                                const int32_t* __restrict__ n_active, int MT, int min_rows,
+                                int4* __restrict__ tiles, int max_tiles,
+                                int32_t* __restrict__ n_tiles) {
+  ffn_plan_n(count, offset, active, *n_active, MT, min_rows, tiles, max_tiles, n_tiles);
 }
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -284,6 +284,15 @@ static int few_rows(int T, int H, int I) {
   return R;
 }
 
+bool ffn_separate_plan(int T, int H, int I, int* MT, int* min_rows) {
+  const int R = few_rows(T, H, I);
+  const int mt = gemm_rows_per_tile(T);
+  if (T <= R || mt == 128) return false;
+  *MT = mt;
+  *min_rows = R + 1;
+  return true;
+}
+
 // A second stream per device for the busy experts' chain (tile plan, grouped GEMMs).  It
 // shares no data with the few-row chain (disjoint experts, so disjoint rows of h and y, and its
 // own workspace regions), so the two run side by side and the caller's stream waits for both.

@@ -348,7 +348,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
     x_to_f16_plan_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(
         a.x, a.x16, n8, a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles, max_tiles,
         n_tiles);
-  } else {
+  } else if (!a.planned) {
     ffn_plan_kernel<<<1, 64, 0, s>>>(a.count, a.offset, a.active, a.n_active, MT, min_rows, tiles,
                                      max_tiles, n_tiles);
   }

@@ -123,9 +123,11 @@ __device__ inline void place_active(const int* cnt, int E, int32_t* __restrict__
 __global__ __launch_bounds__(1024) void group_small_kernel(
     const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ count,
     int32_t* __restrict__ offset, int32_t* __restrict__ sorted_slot,
-    int32_t* __restrict__ slot_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    GroupPlan plan) {
   __shared__ int wcnt[kGroupWaves][kMaxExperts];
   __shared__ __attribute__((aligned(16))) uint32_t key[kMaxExperts];
+  __shared__ int act_l[kMaxExperts];  // the active list, for the tile plan
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int rank[kMaxExperts];
@@ -207,9 +209,18 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
   __syncthreads();
   if (tid < E) {
     const int nact = s_nact;
-    if (key[tid] > 255u) active[rank[tid]] = tid;
+    if (key[tid] > 255u) {
+      active[rank[tid]] = tid;
+      act_l[rank[tid]] = tid;
+    }
     if (tid >= nact) active[tid] = -1;
     if (tid == 0) *n_active = nact;
+  }
+  if (plan.MT > 0) {  // uniform over the block
+    __syncthreads();
+    if (wv == 0)
+      ffn_plan_n(cnt, off, act_l, s_nact, plan.MT, plan.min_rows, plan.tiles, plan.max_tiles,
+                 plan.n_tiles);
   }
 }
 
@@ -284,12 +295,16 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t* __re
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* count,
                         int32_t* offset, int32_t* sorted_slot, int32_t* slot_row,
-                        int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s) {
+                        int32_t* active, int32_t* n_active, int32_t* whist, hipStream_t s,
+                        const GroupPlan* plan) {
   const int n = T * k;
   if (n <= kGroupSmallMax) {
+    GroupPlan p{0, 0, 0, nullptr, nullptr};
+    if (plan) p = *plan;
     group_small_kernel<<<1, 1024, 0, s>>>(ids, n, E, count, offset, sorted_slot, slot_row,
-                                          active, n_active);
+                                          active, n_active, p);
   } else {
+    if (plan && plan->MT > 0) return hipErrorInvalidValue;  // the three-pass grouping plans nothing
     const int nblk = (n + kGroupChunk - 1) / kGroupChunk;
     group_hist_kernel<<<nblk, 1024, 0, s>>>(ids, n, E, whist);
     group_scan_kernel<<<1, 256, 0, s>>>(whist, nblk * kGroupWaves, E, count, offset, active,

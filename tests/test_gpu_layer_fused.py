@@ -129,3 +129,35 @@ def test_fused_layer_falls_back_for_many_tokens():
     L = synth.make_layer(sp, seed=9)
     buf, _ = run_fused(L, sp["k"])
     check_against_oracle(L, sp["k"], buf)
+
+
+# From three tokens up moe_layer_nvfp4 runs route, group, expert FFN and combine in turn, and the
+# one-block grouping also lists the busy experts' row tiles (the FFN call then skips its own
+# planning launch).  Shapes: few-row kernels with busy experts on the side stream (12 tokens),
+# 32-row GEMM tiles (37 and 96 tokens, the latter with a Zipf bias), 64-row tiles (600 tokens).
+FOUR_CALL_SHAPES = {
+    "t12_side_stream": dict(T=12, H=256, I=128, E=8, k=4, router="normal", zipf=None),
+    "t37_rows32": dict(T=37, H=512, I=256, E=16, k=4, router="normal", zipf=None),
+    "t96_zipf": dict(T=96, H=256, I=256, E=64, k=8, router="normal", zipf=1.1),
+    "t600_rows64": dict(T=600, H=256, I=256, E=16, k=4, router="normal", zipf=None),
+}
+
+
+@pytest.mark.parametrize("name", list(FOUR_CALL_SHAPES))
+def test_layer_entry_planned_grouping(name):
+    """moe_layer_nvfp4 above two tokens: parity with the oracle, and bit-identical results to the
+    four public calls made one by one (the same kernels; only the tile plan moves)."""
+    import bit_expert_ffn_amd as moe
+    sp = FOUR_CALL_SHAPES[name]
+    print("case layer entry, planned grouping", name, sp, flush=True)
+    L = synth.make_layer(sp, seed=12)
+    buf, ex = run_fused(L, sp["k"])
+    check_against_oracle(L, sp["k"], buf)
+    T, H = L["x"].shape
+    b4 = moe.LayerBuffers(T, H, sp["I"], sp["E"], sp["k"], device="cuda", y_dtype=torch.float16)
+    bias = None if L["bias"] is None else L["bias"].cuda()
+    moe.layer(L["x"].cuda(), L["w_router"].cuda(), bias, ex, sp["k"], b4)
+    torch.cuda.synchronize()
+    for n in ("topk_id", "topk_w", "count", "offset", "sorted_slot", "slot_row", "active",
+              "n_active", "y", "out"):
+        assert torch.equal(getattr(buf, n), getattr(b4, n)), n
