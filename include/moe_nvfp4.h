@@ -219,7 +219,9 @@ moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *s
  * NULL), topk_id, topk_w, the grouping arrays and out, but not y; the combine there adds each
  * token's experts in the order of the active list rather than by slot.
  * Larger T, or a device that cannot keep one block per CU resident, run the four calls in
- * order, y_dev ([T*k][H] of y_dtype, grouped row order) holding the expert outputs.
+ * order, y_dev ([T*k][H] of y_dtype, grouped row order) holding the expert outputs.  There
+ * the one-block grouping also writes the grouped GEMM's tile list into ws_dev, which saves
+ * the expert-FFN call one launch; every output is bit-identical to that of the four calls.
  * Calls that share ws_dev must not overlap in time. */
 moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const float *bias_dev,
                            const moe_nvfp4_experts *w, int32_t T, int32_t k, float *logits_dev,
