@@ -7,7 +7,9 @@ Prints one JSON line (the benchmark contract) with the layer throughput; the roo
 dominant kernel work, timed with HIP events on the launch stream over the timed region (the
 single-launch kernel, or the expert-FFN call of the four-call path); its HBM traffic from the
 committed PMC summary when the kernel is unchanged since; and the CPU oracle timed on a
-bounded sample.
+bounded sample.  By default every workload below runs in turn, in one process: decode1 gives
+the line's top-level fields and the others the same fields under "legs" (decode1, decode64 and
+prefill16k share one generated expert set).  --workload runs one workload alone.
 
 --combine norm replaces the plain combine with the combine variants (per-expert RMS norm before
 the weighted sum, then the residual update and the next layer's RMS norm) and runs the four-call
@@ -16,7 +18,7 @@ path at every T; the combine call is timed with its own HIP events in both modes
 Workloads (hidden 7168, 256 experts, top-8, NVFP4 experts):
   decode1     T=1, expert intermediate 2048; each step takes the next token of a seeded pool of
               64 tokens, so consecutive steps read different experts (as decoding does) rather
-              than re-reading a set that fits the 256 MB Infinity Cache   [default]
+              than re-reading a set that fits the 256 MB Infinity Cache   [headline]
   decode64    T=64, uniform-random router weights
   verify128   T=128 (8 requests x 16 draft positions), intermediate 256 (one 1/8 shard),
               Zipf(1.1) expert-popularity bias on the logits
@@ -50,49 +52,94 @@ def mx8_expert_bytes(H, I):
     return 3 * (H * I + H * I // 32)
 
 
+LEGS = ("decode1", "decode64", "verify128", "prefill16k")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode1",
-                    choices=["decode1", "decode64", "verify128", "prefill16k"])
+    ap.add_argument("--workload", default="all", choices=("all",) + LEGS,
+                    help="all (default): decode1 is the headline line, the other workloads are "
+                         "reported under 'legs'; else that workload alone")
     ap.add_argument("--combine", default="plain", choices=["plain", "norm"],
                     help="plain: routing-weighted sum; norm: per-expert RMS norm before the sum "
                          "and the residual + next pre-norm epilogue (four-call path)")
     ap.add_argument("--precision", default="nvfp4", choices=["nvfp4", "mx8"],
                     help="mx8: the fp8-compute variant (MXFP8 weights requantised from NVFP4 at "
                          "load time, MXFP8 x and h, scaled matrix cores; four-call path)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="CPU oracle sample budget (0 disables the CPU baseline)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle sample budget per workload (0 disables the CPU baseline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    legs = LEGS if args.workload == "all" else (args.workload,)
+    shared = {}
+    results = {}
+    for wl in legs:
+        results[wl] = run_leg(wl, args, dev, shared)
+        if wl != legs[0]:
+            print("leg %s: %.2f us/layer, roofline frac %s" % (
+                wl, results[wl]["us_per_layer"], results[wl]["roofline"]["frac"]),
+                file=sys.stderr, flush=True)
+    head = results[legs[0]]
+    if len(legs) > 1:
+        head["legs"] = {wl: leg_summary(results[wl]) for wl in legs[1:]}
+    print(json.dumps(head))
+
+
+def leg_summary(r):
+    """The per-workload record under 'legs' of the headline line."""
+    keep = ("value", "unit", "steps", "warmup", "ms_per_step", "us_per_layer", "kernel_us",
+            "dtype", "config", "roofline", "cpu_baseline", "distinct_experts", "layer_hbm_frac",
+            "kernel_algorithmic_bytes", "combine", "ffn_flops")
+    return {k: r[k] for k in keep if k in r}
+
+
+def _experts(sp, dev, shared, seed=0):
+    """Expert weights of a workload (row-major for the oracle's host copy, tile-major for the
+    library), generated once per (H, I, E) and shared by the workloads of the same shape: the
+    generator of every expert is seeded by (seed, expert) alone."""
+    import bit_expert_ffn_amd as moe
+    import synth
+    key = (sp["E"], sp["H"], sp["I"], seed)
+    if key not in shared:
+        shared.clear()  # one weight set resident at a time
+        torch.cuda.empty_cache()
+        raw = synth.make_experts(sp["E"], sp["H"], sp["I"], seed, dev)
+        shared[key] = {"raw": raw, "packed": moe.pack_experts(raw)}
+    return shared[key]
+
+
+def run_leg(wl, args, dev, shared):
     import bit_expert_ffn_amd as moe
     import synth
 
-    wl = args.workload
     sp = dict(synth.SPECS[wl])
     T, H, I, E, k = sp["T"], sp["H"], sp["I"], sp["E"], sp["k"]
     big = wl == "prefill16k"
     steps = args.steps if args.steps is not None else (10 if big else 200)
     warmup = args.warmup if args.warmup is not None else (3 if big else 20)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
 
     print("generating %s inputs on the GPU" % wl, file=sys.stderr, flush=True)
     pool = POOL if T == 1 else 1
-    layer = synth.make_layer(sp, seed=0, device=dev, T=T * pool)
-    xs = layer["x"]
-    wr, bias = layer["w_router"], layer["bias"]
+    seed = 0
+    xs = synth.make_x(T * pool, H, seed, dev)
+    wr = synth.make_router(H, E, sp.get("router", "normal"), seed, dev)
+    bias = synth.make_zipf_bias(E, sp["zipf"], seed, dev) if sp.get("zipf") else None
+    wset = _experts(sp, dev, shared, seed)
+    layer = dict(spec=sp, x=xs, w_router=wr, bias=bias, experts=wset["raw"])
     mx8 = args.precision == "mx8"
     if mx8:  # load-time requantisation to MXFP8 (outside the timed region)
         ex = moe.mx8_experts(layer["experts"])
     else:
-        ex = moe.pack_experts(layer["experts"])  # tile-major copy (load-time conversion)
+        ex = wset["packed"]  # tile-major copy (load-time conversion)
     buf = moe.LayerBuffers(T, H, I, E, k, device=dev, y_dtype=torch.float16, logits=False)
     torch.cuda.synchronize()
 
@@ -150,7 +197,7 @@ def main():
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    print("warmup done; timing %d steps" % steps, file=sys.stderr, flush=True)
+    print("%s: warmup done; timing %d steps" % (wl, steps), file=sys.stderr, flush=True)
 
     # timed region: exactly `steps` layer calls, bracketed by device synchronisation
     # HIP events on the launch stream: around the expert-FFN call of every step (four-call
@@ -170,6 +217,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if fused:
+        moe.layer_check(buf.ws, stream=stream)  # no wait of the single launch gave up
         ffn_ms = ev_all[0].elapsed_time(ev_all[1]) / steps
     else:
         ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
@@ -229,11 +277,13 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = (cpu_baseline_mx8(layer, sp, args.cpu_seconds) if mx8 else
-               cpu_baseline(layer, sp, pool, args.cpu_seconds))
+               cpu_baseline(layer, sp, pool, args.cpu_seconds, shared))
         if norm:
             cpu["combine_norm"] = cpu_combine_norm(T, k, H, min(T, 256))
+    del buf, calls
+    torch.cuda.empty_cache()
 
-    res = {
+    return {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -255,7 +305,6 @@ def main():
         "combine": combine,
         "ffn_flops": flops,
     }
-    print(json.dumps(res))
 
 
 def measured_traffic(kernel_file):
@@ -281,13 +330,19 @@ def measured_traffic(kernel_file):
         return None
 
 
-def cpu_baseline(layer, sp, pool, budget_s):
+def cpu_baseline(layer, sp, pool, budget_s, shared=None):
     """The oracle as it stands, on a bounded sample of the same workload: whole-layer output of
     as many tokens as fit the time budget (at least one), tokens/s."""
     import numpy as np
     import oracle
     print("copying inputs to the host for the CPU oracle", file=sys.stderr, flush=True)
-    ex = oracle.Experts(**{n: v.cpu().numpy() for n, v in layer["experts"].items()})
+    key = "host_experts"
+    if shared is not None and key in shared and shared[key][0] is layer["experts"]:
+        ex = shared[key][1]
+    else:
+        ex = oracle.Experts(**{n: v.cpu().numpy() for n, v in layer["experts"].items()})
+        if shared is not None:
+            shared[key] = (layer["experts"], ex)
     x = layer["x"].cpu().view(torch.int16).numpy().view(np.uint16)
     wr = layer["w_router"].cpu().numpy()
     bias = None if layer["bias"] is None else layer["bias"].cpu().numpy()
@@ -301,8 +356,8 @@ def cpu_baseline(layer, sp, pool, budget_s):
     dt = time.perf_counter() - t0
     return {"value": round(done / dt, 4), "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": "%d token(s) of the %s workload, whole layer per token (fp64 oracle)"
-                      % (done, "decode" if pool > 1 else "same")}
+            "sample": "%d token(s) of the %s workload (T=%d), whole layer per token (fp64 oracle)"
+                      % (done, "decode" if pool > 1 else "same", sp["T"])}
 
 
 def cpu_baseline_mx8(layer, sp, budget_s):

@@ -71,6 +71,8 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_nvfp4_to_mxfp8.restype = i32
         L.moe_nvfp4_to_mxfp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_layer_check.restype = i32
+        L.moe_layer_check.argtypes = [vp, sz, vp]
         L.moe_expert_ffn_mx8.restype = i32
         L.moe_expert_ffn_mx8.argtypes = [vp, ctypes.POINTER(_Mx8Experts), vp, vp, vp, vp, vp,
                                          i32, i32, vp, vp, sz, vp]
@@ -80,7 +82,8 @@ def lib():
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
             "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_norm",
-            "moe_nvfp4_pack", "moe_layer_nvfp4", "moe_nvfp4_to_mxfp8", "moe_expert_ffn_mx8")
+            "moe_nvfp4_pack", "moe_layer_nvfp4", "moe_layer_check", "moe_nvfp4_to_mxfp8",
+            "moe_expert_ffn_mx8")
 
 
 def abi_version():
@@ -347,6 +350,20 @@ def layer_nvfp4(x, w_router, bias, experts, k, buf, stream=None):
     path."""
     prepare_layer_nvfp4(x, w_router, bias, experts, k, buf, stream)()
     return buf.out
+
+
+def layer_check(ws, stream=None):
+    """moe_layer_check: waits for the stream, then raises RuntimeError if a wait inside an
+    earlier single-launch layer call on this workspace gave up (that call's outputs are
+    undefined; the library has cleared the workspace's sync region for the next call)."""
+    _check(lib().moe_layer_check(_dev(ws, "ws", torch.uint8), ws.numel(),
+                                 _stream(stream, ws.device)), "moe_layer_check")
+
+
+def set_layer_spin_limit(ws, polls):
+    """Sets the number of polls after which a wait of the single-launch layer gives up (word 49
+    of the workspace; 0 = the library's default of about 2 s).  Ordered on the current stream."""
+    ws[:256].view(torch.int32)[49] = int(polls)
 
 
 def prepare_layer_nvfp4(x, w_router, bias, experts, k, buf, stream=None):

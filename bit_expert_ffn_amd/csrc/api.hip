@@ -61,6 +61,13 @@ moe_status check_shape(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   return MOE_OK;
 }
 
+// Calls that read x through 32-bit element offsets (T*H) and h through 32-bit element offsets
+// (T*k*I): the grouped GEMMs keep per-lane offsets from a uniform base in 32 bits.
+moe_status check_rows(int64_t T, int64_t H, int64_t I, int64_t k) {
+  if (T * H >= (int64_t)1 << 32 || T * k * I >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 }  // namespace
@@ -71,16 +78,17 @@ MOE_API const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARGUMENT: return "invalid argument (NULL or misaligned pointer, bad size or dtype)";
-    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (E > 256, H or I not a multiple of 128 or above 65536, or T*k >= 2^31)";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (E > 256, H or I not a multiple of 128 or above 65536, T*k >= 2^31, T*H >= 2^32 or T*k*I >= 2^32)";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_INTERNAL: return "internal error";
+    case MOE_ERR_TIMEOUT: return "a wait inside the single-launch layer gave up (outputs undefined; sync region cleared)";
     default: return "unknown status";
   }
 }
 
 MOE_API size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
-  if (check_shape(T, H, I, E, k) != MOE_OK) return 0;
+  if (check_shape(T, H, I, E, k) != MOE_OK || check_rows(T, H, I, k) != MOE_OK) return 0;
   return moe::ws_layout(T, H, I, E, k).total;
 }
 
@@ -160,6 +168,7 @@ static moe_status expert_ffn_run(const void* x_dev, const moe_nvfp4_experts* w,
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st == MOE_OK) st = check_rows(T, w->H, w->I, k);
   if (st != MOE_OK) return st;
   const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
   if (ws_bytes < L.ffn_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -176,6 +185,7 @@ static moe_status expert_ffn_run(const void* x_dev, const moe_nvfp4_experts* w,
   a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
   a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
   a.planned = planned;
+  a.serial = 0;
   int4* tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn(a, tiles, n_tiles, (hipStream_t)stream));
@@ -260,6 +270,7 @@ MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
   if ((bias_dev && !aligned16(bias_dev)) || (logits_dev && !aligned16(logits_dev)))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st == MOE_OK) st = check_rows(T, w->H, w->I, k);
   if (st != MOE_OK) return st;
   const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -370,6 +381,7 @@ MOE_API moe_status moe_expert_ffn_mx8(const void* x_dev, const moe_mx8_experts* 
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape(T, w->H, w->I, w->E, k);
+  if (st == MOE_OK) st = check_rows(T, w->H, w->I, k);
   if (st != MOE_OK) return st;
   if (w->H % 256 != 0 || w->I % 256 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
   const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
@@ -390,4 +402,22 @@ MOE_API moe_status moe_expert_ffn_mx8(const void* x_dev, const moe_mx8_experts* 
   a.tiles = (int4*)(ws + L.mx8_tiles);
   a.n_tiles = (int32_t*)(a.tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn_mx8(a, (hipStream_t)stream));
+}
+
+MOE_API moe_status moe_layer_check(void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!ws_dev || !aligned16(ws_dev)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < moe::kSyncBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(s);
+  uint32_t err = 0;
+  if (e == hipSuccess)
+    e = hipMemcpy(&err, (char*)ws_dev + moe::kSyncErrWord * 4, sizeof(err), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (err == 0) return MOE_OK;
+  // clear the sync region for the next call, except the caller's spin-limit word
+  const size_t spin = (size_t)moe::kSyncSpinWord * 4;
+  e = hipMemsetAsync(ws_dev, 0, spin, s);
+  if (e == hipSuccess) e = hipMemsetAsync((char*)ws_dev + spin + 4, 0, moe::kSyncBytes - spin - 4, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? MOE_ERR_TIMEOUT : MOE_ERR_HIP;
 }

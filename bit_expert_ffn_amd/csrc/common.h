@@ -35,6 +35,11 @@ RoutePlan route_plan(int T, int H, int E);
 // Byte offsets of every call's scratch inside the caller's workspace.  The first kSyncBytes
 // hold the single-launch layer's counters and are used by nothing else.
 constexpr size_t kSyncBytes = 65536;
+// 32-bit words of the sync region that the host reads or writes: the error word (non-zero after
+// a wait of the single-launch kernel gave up) and the spin-limit word (polls before a wait gives
+// up; 0 = the default)
+constexpr int kSyncErrWord = 48;
+constexpr int kSyncSpinWord = 49;
 struct WsLayout {
   size_t route_partial;  // [KS][T][E] fp32
   size_t route_wsplit;   // [3][E][H] bf16 (matrix-core router only)
@@ -84,6 +89,7 @@ struct FfnArgs {
   _Float16* x16;  // workspace
   _Float16* h16;  // workspace
   int planned;    // the tile list of the busy experts is already written (by the grouping)
+  int serial;     // run every kernel on the caller's stream (no side stream, no events)
 };
 hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream_t s);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t* n_tiles,

@@ -293,27 +293,43 @@ bool ffn_separate_plan(int T, int H, int I, int* MT, int* min_rows) {
   return true;
 }
 
-// A second stream per device for the busy experts' chain (tile plan, grouped GEMMs).  It
-// shares no data with the few-row chain (disjoint experts, so disjoint rows of h and y, and its
-// own workspace regions), so the two run side by side and the caller's stream waits for both.
-// Created once per device with the default priority; work of calls from several threads
-// queues on it in order.
-static hipError_t side_stream(hipStream_t* out) {
-  static std::mutex mu;
-  static hipStream_t streams[64];
+// A second stream per device for the busy experts' chain (tile plan, grouped GEMMs), with the
+// two events that fork it from the caller's stream and join it back.  The chain shares no data
+// with the few-row chain (disjoint experts, so disjoint rows of h and y, and its own workspace
+// regions), so the two run side by side and the caller's stream waits for both.  Created once
+// per device, on first use, with the default priority, and kept until the process ends; the
+// mutex is held while a call enqueues its fork, launches and join, so calls from several host
+// threads take turns on the events and queue on the stream in order.
+struct SideChain {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+static std::mutex side_mu;
+
+static hipError_t side_chain(SideChain** out) {
+  static SideChain chains[64];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev]) {
-    err = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+  SideChain& c = chains[dev];
+  if (!c.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&j, hipEventDisableTiming);
     if (err != hipSuccess) {
-      streams[dev] = nullptr;
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (st) (void)hipStreamDestroy(st);
       return err;
     }
+    c.fork = f;
+    c.join = j;
+    c.stream = st;
   }
-  *out = streams[dev];
+  *out = &c;
   return hipSuccess;
 }
 
@@ -323,21 +339,16 @@ hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream
   const bool heavy = a.T > R;  // some expert may have more than R rows
   // both paths present: fork the busy chain onto the side stream, launched first so that its
   // blocks start alongside the few-row kernels
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  hipStream_t side = nullptr;
-  if (R > 0 && heavy) {
-    hipError_t err = side_stream(&side);
-    if (err == hipSuccess) err = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming);
-    if (err == hipSuccess) err = hipEventCreateWithFlags(&ev_join, hipEventDisableTiming);
-    if (err == hipSuccess) err = hipEventRecord(ev_fork, s);
-    if (err == hipSuccess) err = hipStreamWaitEvent(side, ev_fork, 0);
-    if (err == hipSuccess) err = launch_ffn_gemm(a, R + 1, tiles, n_tiles, side);
-    if (err == hipSuccess) err = hipEventRecord(ev_join, side);
-    if (err != hipSuccess) {
-      if (ev_fork) (void)hipEventDestroy(ev_fork);
-      if (ev_join) (void)hipEventDestroy(ev_join);
-      return err;
-    }
+  SideChain* side = nullptr;
+  std::unique_lock<std::mutex> side_lock(side_mu, std::defer_lock);
+  if (R > 0 && heavy && !a.serial) {
+    side_lock.lock();
+    hipError_t err = side_chain(&side);
+    if (err == hipSuccess) err = hipEventRecord(side->fork, s);
+    if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (err == hipSuccess) err = launch_ffn_gemm(a, R + 1, tiles, n_tiles, side->stream);
+    if (err == hipSuccess) err = hipEventRecord(side->join, side->stream);
+    if (err != hipSuccess) return err;
   }
   // with few tokens nearly every expert is few-row: request weights before checking the count
   const int early = (size_t)a.T * a.k <= (size_t)4 * a.E ? 1 : 0;
@@ -393,9 +404,7 @@ hipError_t launch_ffn(const FfnArgs& a, int4* tiles, int32_t* n_tiles, hipStream
   hipError_t err = hipGetLastError();
   if (side) {
     // join: the caller's stream continues once the busy chain is done as well
-    const hipError_t werr = hipStreamWaitEvent(s, ev_join, 0);
-    (void)hipEventDestroy(ev_fork);
-    (void)hipEventDestroy(ev_join);
+    const hipError_t werr = hipStreamWaitEvent(s, side->join, 0);
     return err != hipSuccess ? err : werr;
   }
   if (err != hipSuccess) return err;

@@ -27,13 +27,19 @@
 //   Exit: counter X; the last block to arrive resets the counters and flags for the next call.
 // A barrier: every block adds one to the barrier's counter; the block that completes it raises
 // 16 copies of a flag, and each block polls its own copy.
+// Failure: every wait is bounded (word kLsSyncSpin of the sync region, if non-zero, sets the
+// number of polls; else kLsSpin, about 2 s).  A block whose wait gives up sets the error word,
+// skips the rest of its work and still arrives at counter X, so the last block to exit resets
+// the counters and flags whether or not the call succeeded: a failed call leaves its outputs
+// undefined and the error word set, but cannot leave a barrier half-counted for the next call.
 // Data that crosses blocks (partial logits, h) is written with device-scope stores, which write
 // through the per-XCD L2s (not coherent with each other) to memory, and the counters are relaxed
 // device-scope atomics issued after a full s_waitcnt, so no cache-wide release or acquire is
 // needed.  The readers use plain cached loads: every kernel starts with invalidated caches and
 // no block reads those lines before the counter says they are complete, so the first read on
-// each XCD fetches them from memory and the other blocks of the XCD hit its L2.  Every wait is
-// bounded: on a timeout the block sets the error word and returns.
+// each XCD fetches them from memory and the other blocks of the XCD hit its L2.
+#include <mutex>
+
 #include "common.h"
 #include "dot.h"
 
@@ -43,12 +49,13 @@ constexpr int kLsNS = 32;                 // router: slices of the hidden dimens
 constexpr int kLsEG = 32;                 // router: experts per item
 constexpr int kLsSetC = 4;                // gate/up: chunks per load set
 constexpr int kLsSetD = 8;                // down: chunks per load set
-constexpr uint32_t kLsSpin = 1u << 21;    // polls before a wait gives up (about 2 s)
+constexpr uint32_t kLsSpin = 1u << 21;    // default polls before a wait gives up (about 2 s)
 // Sync region (kSyncBytes at the start of the workspace), in 32-bit words: arrival counters A,
-// C, X and the error word, 64 bytes apart; then kLsFlags copies of the "all arrived" flags of
-// barriers A and C, 4 KB apart so that the pollers of different copies hit different memory
-// channels.
-constexpr int kLsSyncA = 0, kLsSyncC = 16, kLsSyncX = 32, kLsSyncErr = 48;
+// C, X and the error word, 64 bytes apart, the spin-limit word right after the error word;
+// then kLsFlags copies of the "all arrived" flags of barriers A and C, 4 KB apart so that the
+// pollers of different copies hit different memory channels.
+constexpr int kLsSyncA = 0, kLsSyncC = 16, kLsSyncX = 32, kLsSyncErr = kSyncErrWord;
+constexpr int kLsSyncSpin = kSyncSpinWord;
 constexpr int kLsFlags = 16, kLsFlagBase = 64, kLsFlagStride = 1024;
 constexpr int kLsFlagA = 0, kLsFlagC = 16;
 static_assert((kLsFlagBase + (kLsFlags - 1) * kLsFlagStride + kLsFlagC + 1) * 4 <= kSyncBytes,
@@ -76,15 +83,15 @@ __device__ inline void ls_arrive(uint32_t* sync, int ctr, int flag, uint32_t G) 
 }
 
 // Thread 0 polls this block's copy of the flag; the other wavefronts wait at an LDS-only
-// barrier, keeping their own loads in flight.  false (for every thread) after a timeout.
-__device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok) {
+// barrier, keeping their own loads in flight.  false (for every thread) after `limit` polls.
+__device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t limit) {
   if (threadIdx.x == 0) {
     const uint32_t* f = sync + kLsFlagBase + (blockIdx.x % kLsFlags) * kLsFlagStride + flag;
     uint32_t spins = 0;
     int ok = 1;
     while (ld_dev(f) == 0) {
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > kLsSpin) {
+      if (++spins > limit) {
         ok = 0;
         __hip_atomic_fetch_or(sync + kLsSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -96,6 +103,28 @@ __device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok) {
   const bool ok = *s_ok != 0;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return ok;
+}
+
+// Exit, for a block that finished its work or gave up waiting: once this block's stores are
+// complete, thread 0 arrives at counter X; the last block to arrive (every block has then
+// stopped polling) resets the counters and flags for the next call.  The error word and the
+// spin-limit word are left as they are.
+__device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // this block's flag stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint32_t old =
+        __hip_atomic_fetch_add(sync + kLsSyncX, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == G - 1) {
+      st_dev(sync + kLsSyncA, 0u);
+      st_dev(sync + kLsSyncC, 0u);
+      for (int i = 0; i < kLsFlags; ++i) {
+        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
+        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
+      }
+      st_dev(sync + kLsSyncX, 0u);
+    }
+  }
 }
 
 // Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
@@ -144,6 +173,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   const int G = gridDim.x;
   const int T = a.T, H = a.H, I = a.I, E = a.E, k = a.k;
   const int nq = T * k;
+  const uint32_t spin_cfg = a.sync[kLsSyncSpin];  // written by the host before the launch
+  const uint32_t spin = spin_cfg != 0 ? spin_cfg : kLsSpin;
 
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);  // x rows (bf16), staged during barrier A
 
@@ -268,7 +299,10 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   }
 
   // ---- B: logits, top-k, softmax, grouping (every block) ----
-  if (!ls_wait(a.sync, kLsFlagA, &s_flag)) return;
+  if (!ls_wait(a.sync, kLsFlagA, &s_flag, spin)) {
+    ls_exit(a.sync, (uint32_t)G);
+    return;
+  }
   // logits of expert e = tid (slices added in order), kept in registers
   float lg[TT];
 #pragma unroll
@@ -602,7 +636,10 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       // the first weights are requested before waiting for h (not by the polling wavefront,
       // whose poll would queue behind them)
       if (has_k && wv != 0) load_set(qA, sA, 0);
-      if (!ls_wait(a.sync, kLsFlagC, &s_flag)) return;
+      if (!ls_wait(a.sync, kLsFlagC, &s_flag, spin)) {
+        ls_exit(a.sync, (uint32_t)G);
+        return;
+      }
       if (has_k && wv == 0) load_set(qA, sA, 0);
       // both halves of every h row: LDS [half][row][hw_row words].  Plain (cached) loads: no
       // block of this kernel read these lines before counter C, and the caches hold nothing
@@ -683,22 +720,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   }
 
   // ---- exit: the last block resets the counters and flags for the next call ----
-  if (tid == 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // this block's flag stores are complete
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const uint32_t old =
-        __hip_atomic_fetch_add(a.sync + kLsSyncX, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)G - 1) {
-      // every block has passed both barriers: nobody polls these words any more
-      st_dev(a.sync + kLsSyncA, 0u);
-      st_dev(a.sync + kLsSyncC, 0u);
-      for (int i = 0; i < kLsFlags; ++i) {
-        st_dev(a.sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
-        st_dev(a.sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
-      }
-      st_dev(a.sync + kLsSyncX, 0u);
-    }
-  }
+  ls_exit(a.sync, (uint32_t)G);
 }
 
 size_t layer_small_lds(int T, int H, int I, int k) {
@@ -714,10 +736,25 @@ bool layer_small_fits(int T, int H, int I, int E, int k) {
 }
 
 // Blocks of the single-launch kernel on this device: one per CU, provided that at least one
-// block fits per CU (every block must be resident).  0 if not.
+// block fits per CU (every block must be resident); 0 if not.  The answer depends only on the
+// device and the kernel's LDS size, so it is computed once per (device, kernel, LDS size) and
+// cached for the life of the process.
 static int layer_small_grid(int T, bool vec, size_t lds) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int var = (T == 1 ? 0 : 2) + (vec ? 1 : 0);
+  struct Entry {
+    size_t lds;
+    int grid;
+  };
+  static std::mutex mu;
+  static Entry cache[64][4][4];  // [device][kernel][slot]: a few LDS sizes per kernel
+  static int next[64][4];
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& c : cache[dev][var])
+      if (c.grid > 0 && c.lds == lds) return c.grid;
+  }
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -727,7 +764,12 @@ static int layer_small_grid(int T, bool vec, size_t lds) {
                          : (vec ? (const void*)layer_small_kernel<2, true>
                                 : (const void*)layer_small_kernel<2, false>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, 256, lds) != hipSuccess) return 0;
-  return occ >= 1 ? ncu : 0;
+  const int grid = occ >= 1 ? ncu : 0;
+  if (grid > 0) {
+    std::lock_guard<std::mutex> lock(mu);
+    cache[dev][var][next[dev][var]++ % 4] = Entry{lds, grid};
+  }
+  return grid;
 }
 
 hipError_t launch_layer_small(const LayerSmallArgs& a, hipStream_t s) {

@@ -28,10 +28,14 @@
  *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA tensors); everything
  *     else is host memory read during the call.  Device pointers must be 16-byte aligned.
  *     Arrays are dense, row-major, with the last index contiguous.
- *   - Ownership: the caller allocates and frees every buffer.  The library never allocates,
- *     frees or keeps a pointer after a call returns; kernels still queued on `stream` read and
- *     write the buffers until they finish.  The library holds no state and calls may come from
- *     any thread; calls that share a workspace must be ordered on one stream.
+ *   - Ownership: the caller allocates and frees every buffer.  The library never allocates
+ *     device memory for a call, frees nothing of the caller's and keeps no pointer after a call
+ *     returns; kernels still queued on `stream` read and write the buffers until they finish.
+ *     Calls may come from any thread; calls that share a workspace must be ordered on one
+ *     stream.  The library keeps no per-call state.  Per device, on first use, it creates and
+ *     keeps until the process ends: one side stream and two events (moe_expert_ffn_nvfp4 forks
+ *     its busy-expert chain onto them for 3..31 tokens), and the single-launch kernel's
+ *     occupancy.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is asynchronous: it
  *     validates its arguments on the host, enqueues kernels on `stream` and returns.  There is
  *     no host-device synchronisation inside any call.
@@ -41,7 +45,11 @@
  *     (they come from moe_route); ids outside [0, E) are undefined behaviour.  NaN/Inf inputs
  *     propagate; there are no device-side checks.
  *   - Shape limits: 1 <= k <= E <= 256; H and I multiples of 128 with 128 <= H, I <= 65536;
- *     T >= 1 and T*k < 2^31.
+ *     T >= 1 and T*k < 2^31; for the calls that take I, also T*H < 2^32 and T*k*I < 2^32.
+ *   - Activation range: on the matrix-core path (32 tokens and more) x enters the matrix cores
+ *     as f16, so |x| must not exceed 65504 (larger values become Inf there, while the few-row
+ *     and single-launch paths, which dot x as bf16, stay finite); magnitudes below 2^-14 lose
+ *     precision as f16 subnormals.
  */
 #ifndef MOE_NVFP4_H
 #define MOE_NVFP4_H
@@ -53,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 4
+#define MOE_NVFP4_ABI_VERSION 5
 
 typedef int32_t moe_status;
 enum {
@@ -62,7 +70,8 @@ enum {
   MOE_ERR_UNSUPPORTED_SHAPE = -2,  /* H or I not a multiple of 128, E > 256, sizes too large   */
   MOE_ERR_WORKSPACE_TOO_SMALL = -3,
   MOE_ERR_HIP = -4,                /* a HIP launch or runtime call failed                      */
-  MOE_ERR_INTERNAL = -5
+  MOE_ERR_INTERNAL = -5,
+  MOE_ERR_TIMEOUT = -6             /* moe_layer_check: a wait of the single-launch layer gave up */
 };
 
 /* element type tag of the expert-output buffer y */
@@ -104,10 +113,12 @@ const char *moe_status_string(moe_status status);
  * outside the shape limits.  Apart from its first 64 KiB the contents are scratch: calls keep
  * nothing there from one call to the next.  The first 64 KiB hold the counters and flags of
  * moe_layer_nvfp4's single-launch path: they must be zero before the first moe_layer_nvfp4 call
- * on the buffer (for example, allocate it zero-filled), every completed call leaves them zero,
- * and no other call reads or writes them.  Word 48 (bytes 192..195) becomes non-zero only if a
- * wait inside the single-launch kernel timed out; the call's outputs are then undefined and
- * the 64 KiB must be zeroed again. */
+ * on the buffer (for example, allocate it zero-filled), every call leaves the counters and
+ * flags zero, and no other call reads or writes them.  Two 32-bit words there are the
+ * caller's: word 48 (bytes 192..195), the error word, becomes non-zero if a wait inside the
+ * single-launch kernel gave up (that call's outputs are then undefined; moe_layer_check reads
+ * and clears it); word 49 (bytes 196..199), if non-zero, is the number of polls after which
+ * such a wait gives up (0: the default, about 2 s). */
 size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /* Router and top-k ("The model": every token is routed to k of E experts).
@@ -214,10 +225,15 @@ moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *s
  * every token's expert weights are requested as soon as its routing is known and no launch
  * gap separates the steps ("Optimizing Muse Spark Open on TPU v7 with SGLang-TorchTPU",
  * section 1 "A megakernel", section 2 "Pipelining everything inside the megakernel").  The
- * kernel keeps one block per CU resident and its blocks wait for each other through the
- * counters at the start of ws_dev (see moe_workspace_size).  That path writes logits (if not
- * NULL), topk_id, topk_w, the grouping arrays and out, but not y; the combine there adds each
- * token's experts in the order of the active list rather than by slot.
+ * kernel launches one block per CU and its blocks wait for each other through the counters at
+ * the start of ws_dev (see moe_workspace_size).  Precondition: every block must become
+ * resident while the others wait, so no other work may hold the device's CUs for the length
+ * of a wait (about 2 s by default) -- for example a long kernel on another stream.  If a wait
+ * gives up, its block skips the rest of its work, the call's outputs are undefined, the error
+ * word is set (moe_layer_check reports it) and the counters are still reset for the next call.
+ * That path writes logits (if not NULL), topk_id, topk_w, the grouping arrays and out, but not
+ * y; the combine there adds each token's experts in the order of the active list rather than
+ * by slot.
  * Larger T, or a device that cannot keep one block per CU resident, run the four calls in
  * order, y_dev ([T*k][H] of y_dtype, grouped row order) holding the expert outputs.  There
  * the one-block grouping also writes the grouped GEMM's tile list into ws_dev, which saves
@@ -230,6 +246,14 @@ moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const f
                            int32_t *active_dev, int32_t *n_active_dev, void *y_dev,
                            int32_t y_dtype, float *out_dev, void *ws_dev, size_t ws_bytes,
                            void *stream);
+
+/* Status of the single-launch layer on this workspace: waits until `stream` is idle, reads the
+ * error word (word 48 of ws_dev) and returns MOE_OK if it is zero.  Otherwise a wait inside an
+ * earlier moe_layer_nvfp4 call on this workspace gave up (the outputs of that call are
+ * undefined): the call clears the first 64 KiB of ws_dev except word 49 (the spin limit) and
+ * returns MOE_ERR_TIMEOUT.  Synchronising; pass the stream the layer calls were made on.
+ * ws_dev must be 16-byte aligned and ws_bytes >= 65536. */
+moe_status moe_layer_check(void *ws_dev, size_t ws_bytes, void *stream);
 
 /* ---- fp8-compute variant ------------------------------------------------------------------
  * The pages' serving stack computes in fp8 with NVFP4 expert weights ("Optimizing Muse Spark

@@ -71,6 +71,31 @@ def check_out(g, r, max_rel=MAX_REL, mae=MAE):
     return mr, ma
 
 
+def selection_weights(ids, logits_row):
+    """Softmax over the oracle's logits of a given selection (fp64)."""
+    l = logits_row[list(ids)].astype(np.float64)
+    p = np.exp(l - l.max())
+    return p / p.sum()
+
+
+def oracle_on_selection(x_bits, ex, ref, exempt, k):
+    """The oracle's grouping, expert rows and combine on the selection the comparison accepts:
+    the oracle's own ids, except near-tie tokens whose GPU ids are one of the alternatives that
+    check_routing derived from the oracle's logits (weights then recomputed from the oracle's
+    logits).  Returns (ids, w, grouping, y, out)."""
+    ids = ref["topk_id"].copy()
+    w = np.array(ref["topk_w"], np.float64)
+    for t, sel in exempt.items():
+        ids[t] = sel
+        w[t] = selection_weights(sel, ref["logits"][t])
+    if not exempt:
+        return ids, w, ref["group"], ref["y"], ref["out"]
+    grp = oracle.group(ids, ex.E)
+    y = oracle.ffn(x_bits, ex, grp, k)
+    out = oracle.combine(y, grp["slot_row"], w, k, ex.H)
+    return ids, w, grp, y, out
+
+
 def oracle_token_out(x_bits, ex, t, ids, logits_row):
     """Oracle output of token t for a given selection (used for near-tie alternatives)."""
     l = logits_row[list(ids)].astype(np.float64)

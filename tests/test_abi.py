@@ -31,13 +31,16 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.abi_version() == 4
-    for code in (OK, INVALID, SHAPE, WS, -4, -5, 7):
+    assert moe.abi_version() == 5
+    for code in (OK, INVALID, SHAPE, WS, -4, -5, -6, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
 
 
 @pytest.mark.parametrize("T,H,I,E,k,ok", [
     (1, 7168, 2048, 256, 8, True), (4, 256, 128, 8, 2, True), (16384, 7168, 2048, 256, 8, True),
+    # x and h are read through 32-bit element offsets: T*H and T*k*I below 2^32
+    (65536, 65536, 128, 8, 2, False), (65535, 65536, 128, 8, 2, True),
+    (262144, 256, 2048, 256, 8, False), (262143, 256, 2048, 256, 8, True),
     (0, 256, 128, 8, 2, False), (4, 250, 128, 8, 2, False), (4, 256, 100, 8, 2, False),
     (4, 256, 128, 300, 2, False), (4, 256, 128, 8, 9, False), (4, 256, 128, 8, 0, False),
 ])
@@ -225,6 +228,22 @@ def test_layer_rejects_bad_arguments():
     assert _layer(ex=moe._Experts(A, A, A, A, A, A, None, 8, 256, 128)) == INVALID
     assert _layer(ex=moe._Experts(A, A, A, A, A, A, A, 8, 250, 128)) == SHAPE
     assert _layer(ws_bytes=1024) == WS
+
+
+def test_ffn_and_layer_reject_offsets_beyond_32_bits():
+    # T*k*I = 2^32: the down GEMM's h offsets would wrap
+    big = _experts(E=256, H=256, I=2048)
+    assert _ffn(big, T=262144, k=8) == SHAPE
+    assert _layer(ex=moe._Experts(A, A, A, A, A, A, A, 256, 256, 2048), T=262144, k=8) == SHAPE
+    ex = moe._Mx8Experts(A, A, A, A, A, A, 256, 256, 2048)
+    assert _mx8(ex=ex, T=262144, k=8) == SHAPE
+
+
+def test_layer_check_rejects_bad_arguments():
+    c = moe.lib().moe_layer_check
+    assert c(None, 1 << 20, None) == INVALID
+    assert c(A + 4, 1 << 20, None) == INVALID
+    assert c(A, 1024, None) == WS
 
 
 def test_workspace_leaves_room_for_the_sync_words():

@@ -161,3 +161,40 @@ def test_layer_entry_planned_grouping(name):
     for n in ("topk_id", "topk_w", "count", "offset", "sorted_slot", "slot_row", "active",
               "n_active", "y", "out"):
         assert torch.equal(getattr(buf, n), getattr(b4, n)), n
+
+
+@pytest.mark.parametrize("name", ["t1_tiny", "t2_small"])
+@pytest.mark.parametrize("word", [0, 16])
+def test_fused_layer_gives_up_and_recovers(name, word):
+    """A barrier that cannot complete, forced from the host: arrival counter A (word 0) or C
+    (word 16) preset far above the grid size, so no arrival completes it, with a short spin
+    limit (word 49).  Every block must give up, still arrive at the exit counter and leave the
+    counters and flags reset; the error word is set and moe_layer_check reports it and clears
+    it; the next call on the same workspace is correct again, bit for bit."""
+    import bit_expert_ffn_amd as moe
+    sp = SHAPES[name]
+    print("case fused give-up", name, "word", word, flush=True)
+    L = synth.make_layer(sp, seed=13)
+    buf, ex = run_fused(L, sp["k"])
+    moe.layer_check(buf.ws)
+    first = {n: getattr(buf, n).clone() for n in ("out", "topk_id", "topk_w")}
+    words = buf.ws[:65536].view(torch.int32)
+    moe.set_layer_spin_limit(buf.ws, 2000)
+    words[word] = 1 << 30
+    buf.out.fill_(-1.0)
+    run_fused(L, sp["k"], buf=buf, ex=ex)  # synchronises: every block has exited
+    w = sync_words(buf)
+    assert w[48] != 0, "error word not set"
+    assert w[49] == 2000
+    rest = np.delete(w, [48, 49])
+    assert not rest.any(), "counters or flags left set: words %s" % np.nonzero(rest)[0][:8]
+    with pytest.raises(RuntimeError, match="moe_layer_check"):
+        moe.layer_check(buf.ws)
+    w = sync_words(buf)
+    assert w[48] == 0 and w[49] == 2000
+    moe.set_layer_spin_limit(buf.ws, 0)
+    run_fused(L, sp["k"], buf=buf, ex=ex)
+    moe.layer_check(buf.ws)
+    assert not np.any(sync_words(buf))
+    for n, v in first.items():
+        assert torch.equal(getattr(buf, n), v), n
