@@ -29,9 +29,10 @@
 // 16 copies of a flag, and each block polls its own copy.
 // Failure: every wait is bounded (word kLsSyncSpin of the sync region, if non-zero, sets the
 // number of polls; else kLsSpin, about 2 s).  A block whose wait gives up sets the error word,
-// skips the rest of its work and still arrives at counter X, so the last block to exit resets
-// the counters and flags whether or not the call succeeded: a failed call leaves its outputs
-// undefined and the error word set, but cannot leave a barrier half-counted for the next call.
+// writes NaN over its output tiles, skips the rest of its work and still arrives at counter X,
+// so the last block to exit resets the counters and flags whether or not the call succeeded: a
+// failed call leaves NaN in out and the error word set, but cannot leave a barrier
+// half-counted for the next call.
 // Data that crosses blocks (partial logits, h) is written with device-scope stores, which write
 // through the per-XCD L2s (not coherent with each other) to memory, and the counters are relaxed
 // device-scope atomics issued after a full s_waitcnt, so no cache-wide release or acquire is
@@ -125,6 +126,16 @@ __device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
       st_dev(sync + kLsSyncX, 0u);
     }
   }
+}
+
+// A block that gave up waiting writes NaN over its output tiles (the 32-feature tiles
+// blockIdx.x + m * G of every token), so a failed call shows in out: a give-up at barrier A
+// keeps barrier A or C from completing for everyone, so every block with output tiles gives up.
+__device__ inline void ls_fail_out(const LayerSmallArgs& a, int G) {
+  const float nan = __builtin_nanf("");
+  for (int ftp = blockIdx.x; ftp < a.H / 32; ftp += G)
+    for (int i = threadIdx.x; i < a.T * 32; i += 256)
+      a.out[(size_t)(i >> 5) * a.H + ftp * 32 + (i & 31)] = nan;
 }
 
 // Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
@@ -300,6 +311,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
 
   // ---- B: logits, top-k, softmax, grouping (every block) ----
   if (!ls_wait(a.sync, kLsFlagA, &s_flag, spin)) {
+    ls_fail_out(a, G);
     ls_exit(a.sync, (uint32_t)G);
     return;
   }
@@ -637,6 +649,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       // whose poll would queue behind them)
       if (has_k && wv != 0) load_set(qA, sA, 0);
       if (!ls_wait(a.sync, kLsFlagC, &s_flag, spin)) {
+        ls_fail_out(a, G);
         ls_exit(a.sync, (uint32_t)G);
         return;
       }

@@ -229,8 +229,10 @@ moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *s
  * the start of ws_dev (see moe_workspace_size).  Precondition: every block must become
  * resident while the others wait, so no other work may hold the device's CUs for the length
  * of a wait (about 2 s by default) -- for example a long kernel on another stream.  If a wait
- * gives up, its block skips the rest of its work, the call's outputs are undefined, the error
- * word is set (moe_layer_check reports it) and the counters are still reset for the next call.
+ * gives up, its block writes NaN over its features of out and skips the rest of its work (any
+ * give-up keeps a barrier from completing for every block that has out features, so out shows
+ * NaN; the other outputs are undefined), the error word is set (moe_layer_check reports it) and
+ * the counters are still reset for the next call.
  * That path writes logits (if not NULL), topk_id, topk_w, the grouping arrays and out, but not
  * y; the combine there adds each token's experts in the order of the active list rather than
  * by slot.

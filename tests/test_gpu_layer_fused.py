@@ -168,9 +168,10 @@ def test_layer_entry_planned_grouping(name):
 def test_fused_layer_gives_up_and_recovers(name, word):
     """A barrier that cannot complete, forced from the host: arrival counter A (word 0) or C
     (word 16) preset far above the grid size, so no arrival completes it, with a short spin
-    limit (word 49).  Every block must give up, still arrive at the exit counter and leave the
-    counters and flags reset; the error word is set and moe_layer_check reports it and clears
-    it; the next call on the same workspace is correct again, bit for bit."""
+    limit (word 49).  Every block must give up, write NaN over its features of out, still arrive
+    at the exit counter and leave the counters and flags reset; the error word is set and
+    moe_layer_check reports it and clears it; the next call on the same workspace is correct
+    again, bit for bit."""
     import bit_expert_ffn_amd as moe
     sp = SHAPES[name]
     print("case fused give-up", name, "word", word, flush=True)
@@ -183,6 +184,7 @@ def test_fused_layer_gives_up_and_recovers(name, word):
     words[word] = 1 << 30
     buf.out.fill_(-1.0)
     run_fused(L, sp["k"], buf=buf, ex=ex)  # synchronises: every block has exited
+    assert torch.isnan(buf.out).all(), "blocks that gave up must write NaN over their features"
     w = sync_words(buf)
     assert w[48] != 0, "error word not set"
     assert w[49] == 2000
