@@ -71,6 +71,10 @@ def lib():
                                       vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_nvfp4_to_mxfp8.restype = i32
         L.moe_nvfp4_to_mxfp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_layer_nvfp4_noalloc.restype = i32
+        L.moe_layer_nvfp4_noalloc.argtypes = [vp, vp, vp, ctypes.POINTER(_Experts), i32, i32,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                              vp]
         L.moe_layer_check.restype = i32
         L.moe_layer_check.argtypes = [vp, sz, vp]
         L.moe_expert_ffn_mx8.restype = i32
@@ -82,8 +86,8 @@ def lib():
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
             "moe_group", "moe_expert_ffn_nvfp4", "moe_combine", "moe_combine_norm",
-            "moe_nvfp4_pack", "moe_layer_nvfp4", "moe_layer_check", "moe_nvfp4_to_mxfp8",
-            "moe_expert_ffn_mx8")
+            "moe_nvfp4_pack", "moe_layer_nvfp4", "moe_layer_nvfp4_noalloc", "moe_layer_check",
+            "moe_nvfp4_to_mxfp8", "moe_expert_ffn_mx8")
 
 
 def abi_version():
@@ -349,6 +353,34 @@ def layer_nvfp4(x, w_router, bias, experts, k, buf, stream=None):
     tokens).  Results are left in `buf` like layer(); buf.y is written only by the four-call
     path."""
     prepare_layer_nvfp4(x, w_router, bias, experts, k, buf, stream)()
+    return buf.out
+
+
+def layer_nvfp4_noalloc(x, w_router, bias, experts, k, buf, stream=None):
+    """moe_layer_nvfp4_noalloc: as layer_nvfp4, with the library's own per-GPU scratch instead of
+    buf.ws (which is not used).  Results are left in `buf`."""
+    T, H = x.shape
+    s = experts_struct(experts)
+    E = s.E
+    if s.H != H or w_router.shape != (H, E):
+        raise ValueError("x, w_router and experts disagree on H or E")
+    y = buf.y
+    yd = MOE_F16 if y.dtype == torch.float16 else MOE_F32
+    n = T * k
+    args = (_dev(x, "x", torch.bfloat16), _dev(w_router, "w_router", torch.float32, (H, E)),
+            None if bias is None else _dev(bias, "bias", torch.float32, (E,)), ctypes.byref(s),
+            T, k, None if buf.logits is None else _dev(buf.logits, "logits", torch.float32, (T, E)),
+            _dev(buf.topk_id, "topk_id", torch.int32, (T, k)),
+            _dev(buf.topk_w, "topk_w", torch.float32, (T, k)),
+            _dev(buf.count, "count", torch.int32, (E,)),
+            _dev(buf.offset, "offset", torch.int32, (E + 1,)),
+            _dev(buf.sorted_slot, "sorted_slot", torch.int32, (n,)),
+            _dev(buf.slot_row, "slot_row", torch.int32, (n,)),
+            _dev(buf.active, "active", torch.int32, (E,)),
+            _dev(buf.n_active, "n_active", torch.int32, (1,)),
+            _dev(y, "y", y.dtype, (n, H)), yd, _dev(buf.out, "out", torch.float32, (T, H)),
+            _stream(stream, x.device))
+    _check(lib().moe_layer_nvfp4_noalloc(*args), "moe_layer_nvfp4_noalloc")
     return buf.out
 
 

@@ -3,6 +3,8 @@
 // check returns an error code and launches nothing.
 #include "../../include/moe_nvfp4.h"
 
+#include <mutex>
+
 #include "common.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -82,6 +84,7 @@ MOE_API const char* moe_status_string(moe_status s) {
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_INTERNAL: return "internal error";
+    case MOE_ERR_SCRATCH_TOO_SMALL: return "the layer needs more scratch than moe_layer_nvfp4_noalloc holds (moe_workspace_size above 16 MiB)";
     case MOE_ERR_TIMEOUT: return "a wait inside the single-launch layer gave up (outputs undefined; sync region cleared)";
     default: return "unknown status";
   }
@@ -154,7 +157,7 @@ static moe_status expert_ffn_run(const void* x_dev, const moe_nvfp4_experts* w,
                                  const int32_t* sorted_slot_dev, const int32_t* active_dev,
                                  const int32_t* n_active_dev, int32_t T, int32_t k, void* y_dev,
                                  int32_t y_dtype, void* ws_dev, size_t ws_bytes, void* stream,
-                                 int planned) {
+                                 int planned, int serial) {
   if (!x_dev || !w || !count_dev || !offset_dev || !sorted_slot_dev || !active_dev ||
       !n_active_dev || !y_dev || !ws_dev)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -185,7 +188,7 @@ static moe_status expert_ffn_run(const void* x_dev, const moe_nvfp4_experts* w,
   a.x16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_x16);
   a.h16 = reinterpret_cast<_Float16*>((char*)ws_dev + L.ffn_h16);
   a.planned = planned;
-  a.serial = 0;
+  a.serial = serial;
   int4* tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + moe::gemm_max_tiles(T, k, w->E));
   return from_hip(moe::launch_ffn(a, tiles, n_tiles, (hipStream_t)stream));
@@ -198,7 +201,7 @@ MOE_API moe_status moe_expert_ffn_nvfp4(const void* x_dev, const moe_nvfp4_exper
                                         void* y_dev, int32_t y_dtype, void* ws_dev,
                                         size_t ws_bytes, void* stream) {
   return expert_ffn_run(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
-                        n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream, 0);
+                        n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream, 0, 0);
 }
 
 MOE_API moe_status moe_combine(const void* y_dev, int32_t y_dtype, const int32_t* slot_row_dev,
@@ -245,14 +248,15 @@ MOE_API moe_status moe_combine_norm(const void* y_dev, int32_t y_dtype,
   return from_hip(moe::launch_combine_norm(a, y_dtype == MOE_F16, (hipStream_t)stream));
 }
 
-MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
-                                   const float* bias_dev, const moe_nvfp4_experts* w, int32_t T,
-                                   int32_t k, float* logits_dev, int32_t* topk_id_dev,
-                                   float* topk_w_dev, int32_t* count_dev, int32_t* offset_dev,
-                                   int32_t* sorted_slot_dev, int32_t* slot_row_dev,
-                                   int32_t* active_dev, int32_t* n_active_dev, void* y_dev,
-                                   int32_t y_dtype, float* out_dev, void* ws_dev,
-                                   size_t ws_bytes, void* stream) {
+// moe_layer_nvfp4 on a given scratch buffer; serial: no side stream or events (every kernel on
+// `stream`), for the allocation-free entry point
+static moe_status layer_run(const void* x_dev, const float* w_router_dev, const float* bias_dev,
+                            const moe_nvfp4_experts* w, int32_t T, int32_t k, float* logits_dev,
+                            int32_t* topk_id_dev, float* topk_w_dev, int32_t* count_dev,
+                            int32_t* offset_dev, int32_t* sorted_slot_dev, int32_t* slot_row_dev,
+                            int32_t* active_dev, int32_t* n_active_dev, void* y_dev,
+                            int32_t y_dtype, float* out_dev, void* ws_dev, size_t ws_bytes,
+                            void* stream, int serial, moe_status too_small) {
   if (!x_dev || !w_router_dev || !w || !topk_id_dev || !topk_w_dev || !count_dev ||
       !offset_dev || !sorted_slot_dev || !slot_row_dev || !active_dev || !n_active_dev ||
       !y_dev || !out_dev || !ws_dev)
@@ -273,7 +277,7 @@ MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
   if (st == MOE_OK) st = check_rows(T, w->H, w->I, k);
   if (st != MOE_OK) return st;
   const moe::WsLayout L = moe::ws_layout(T, w->H, w->I, w->E, k);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < L.total) return too_small;
   const int H = w->H, I = w->I, E = w->E;
   if (moe::layer_small_fits(T, H, I, E, k)) {
     moe::LayerSmallArgs a;
@@ -314,9 +318,76 @@ MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
   if (st != MOE_OK) return st;
   st = expert_ffn_run(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
                       n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream,
-                      fuse ? 1 : 0);
+                      fuse ? 1 : 0, serial);
   if (st != MOE_OK) return st;
   return moe_combine(y_dev, y_dtype, slot_row_dev, topk_w_dev, T, k, H, out_dev, stream);
+}
+
+MOE_API moe_status moe_layer_nvfp4(const void* x_dev, const float* w_router_dev,
+                                   const float* bias_dev, const moe_nvfp4_experts* w, int32_t T,
+                                   int32_t k, float* logits_dev, int32_t* topk_id_dev,
+                                   float* topk_w_dev, int32_t* count_dev, int32_t* offset_dev,
+                                   int32_t* sorted_slot_dev, int32_t* slot_row_dev,
+                                   int32_t* active_dev, int32_t* n_active_dev, void* y_dev,
+                                   int32_t y_dtype, float* out_dev, void* ws_dev,
+                                   size_t ws_bytes, void* stream) {
+  return layer_run(x_dev, w_router_dev, bias_dev, w, T, k, logits_dev, topk_id_dev, topk_w_dev,
+                   count_dev, offset_dev, sorted_slot_dev, slot_row_dev, active_dev,
+                   n_active_dev, y_dev, y_dtype, out_dev, ws_dev, ws_bytes, stream, 0,
+                   MOE_ERR_WORKSPACE_TOO_SMALL);
+}
+
+// ---- allocation-free variant of moe_layer_nvfp4 ----
+// Its scratch is this file-scope device array (one copy per GPU, held until the process ends).
+// In host code the array's name is only a host-side stand-in: its device address on the current
+// device comes from hipGetSymbolAddress, taken once per device on the first call there and
+// kept; every kernel argument uses that address.  The first kSyncBytes (the single-launch
+// kernel's counters and flags) start zero at load, and every call leaves them zero (a call
+// whose waits give up included), so nothing needs clearing per call.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[64];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+MOE_API moe_status moe_layer_nvfp4_noalloc(const void* x_dev, const float* w_router_dev,
+                                           const float* bias_dev, const moe_nvfp4_experts* w,
+                                           int32_t T, int32_t k, float* logits_dev,
+                                           int32_t* topk_id_dev, float* topk_w_dev,
+                                           int32_t* count_dev, int32_t* offset_dev,
+                                           int32_t* sorted_slot_dev, int32_t* slot_row_dev,
+                                           int32_t* active_dev, int32_t* n_active_dev,
+                                           void* y_dev, int32_t y_dtype, float* out_dev,
+                                           void* stream) {
+  // shapes that need more scratch than the array holds are refused before any HIP call
+  if (w && check_shape(T, w->H, w->I, w->E, k) == MOE_OK &&
+      check_rows(T, w->H, w->I, k) == MOE_OK &&
+      moe::ws_layout(T, w->H, w->I, w->E, k).total > kNoAllocScratchBytes)
+    return MOE_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return layer_run(x_dev, w_router_dev, bias_dev, w, T, k, logits_dev, topk_id_dev, topk_w_dev,
+                   count_dev, offset_dev, sorted_slot_dev, slot_row_dev, active_dev,
+                   n_active_dev, y_dev, y_dtype, out_dev, ws, kNoAllocScratchBytes, stream, 1,
+                   MOE_ERR_SCRATCH_TOO_SMALL);
 }
 
 MOE_API moe_status moe_nvfp4_pack(const uint8_t* q_rowmajor_dev, const uint8_t* s_rowmajor_dev,

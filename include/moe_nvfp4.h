@@ -71,7 +71,8 @@ enum {
   MOE_ERR_WORKSPACE_TOO_SMALL = -3,
   MOE_ERR_HIP = -4,                /* a HIP launch or runtime call failed                      */
   MOE_ERR_INTERNAL = -5,
-  MOE_ERR_TIMEOUT = -6             /* moe_layer_check: a wait of the single-launch layer gave up */
+  MOE_ERR_TIMEOUT = -6,            /* moe_layer_check: a wait of the single-launch layer gave up */
+  MOE_ERR_SCRATCH_TOO_SMALL = -7   /* moe_layer_nvfp4_noalloc: the shape needs more than 16 MiB */
 };
 
 /* element type tag of the expert-output buffer y */
@@ -248,6 +249,29 @@ moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const f
                            int32_t *active_dev, int32_t *n_active_dev, void *y_dev,
                            int32_t y_dtype, float *out_dev, void *ws_dev, size_t ws_bytes,
                            void *stream);
+
+/* moe_layer_nvfp4 without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, outputs and meaning as moe_layer_nvfp4 minus ws_dev / ws_bytes; the caller still
+ * passes every input and output buffer.  The scratch is a 16 MiB array of device memory that
+ * the library holds per GPU from its first use there until the process ends; a call whose
+ * moe_workspace_size(T, H, I, E, k) exceeds 16 MiB returns MOE_ERR_SCRATCH_TOO_SMALL and
+ * launches nothing (at H = 7168, I = 2048, E = 256, k = 8 that is above about 340 tokens).
+ * The call makes no device allocation or free, no library call that allocates, creates no
+ * stream or event (every kernel, also the busy-expert chain of 3..31 tokens, runs on `stream`),
+ * and the first call on a device only looks up the array's address there.  The array keeps
+ * the last call's contents; the only part that must start zero -- the single-launch kernel's
+ * counters and flags -- is zero at load and left zero by every call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two streams, two threads
+ * without ordering) race and give undefined results.  A single-launch wait that gives up shows
+ * as NaN in out (see moe_layer_nvfp4); its error word is not readable by the caller. */
+moe_status moe_layer_nvfp4_noalloc(const void *x_dev, const float *w_router_dev,
+                                   const float *bias_dev, const moe_nvfp4_experts *w, int32_t T,
+                                   int32_t k, float *logits_dev, int32_t *topk_id_dev,
+                                   float *topk_w_dev, int32_t *count_dev, int32_t *offset_dev,
+                                   int32_t *sorted_slot_dev, int32_t *slot_row_dev,
+                                   int32_t *active_dev, int32_t *n_active_dev, void *y_dev,
+                                   int32_t y_dtype, float *out_dev, void *stream);
 
 /* Status of the single-launch layer on this workspace: waits until `stream` is idle, reads the
  * error word (word 48 of ws_dev) and returns MOE_OK if it is zero.  Otherwise a wait inside an

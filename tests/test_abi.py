@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert moe.abi_version() == 5
-    for code in (OK, INVALID, SHAPE, WS, -4, -5, -6, 7):
+    for code in (OK, INVALID, SHAPE, WS, -4, -5, -6, -7, 7):
         assert isinstance(moe.status_string(code), str) and moe.status_string(code)
 
 
@@ -250,3 +250,12 @@ def test_workspace_leaves_room_for_the_sync_words():
     # the single-launch layer's counters and flags occupy the first 64 KiB; every region follows
     for T in (1, 2, 64):
         assert moe.workspace_size(T, 7168, 2048, 256, 8) >= 65536 + T * 7168 * 2
+
+
+def test_layer_noalloc_refuses_shapes_beyond_its_scratch():
+    # refused on the host, before the library looks up its scratch array on the device
+    ex = moe._Experts(A, A, A, A, A, A, A, 256, 7168, 2048)
+    assert moe.workspace_size(4096, 7168, 2048, 256, 8) > 16 << 20
+    st = moe.lib().moe_layer_nvfp4_noalloc(A, A, None, ctypes.byref(ex), 4096, 8, None, A, A, A,
+                                           A, A, A, A, A, A, 1, A, None)
+    assert st == -7
