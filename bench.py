@@ -1,19 +1,22 @@
 """Benchmark of one NVFP4 sparse-MoE FFN layer on one MI355X.
 
 A step is one pass of the whole layer over one batch of seeded synthetic tokens whose inputs
-are already resident in HBM: for one or two tokens one moe_layer_nvfp4 call (a single
-persistent kernel), otherwise moe_route -> moe_group -> moe_expert_ffn_nvfp4 -> moe_combine.
-Prints one JSON line (the benchmark contract) with the layer throughput; the roofline of the
-dominant kernel work, timed with HIP events on the launch stream over the timed region (the
-single-launch kernel, or the expert-FFN call of the four-call path); its HBM traffic from the
-committed PMC summary when the kernel is unchanged since; and the CPU oracle timed on a
-bounded sample.  By default every workload below runs in turn, in one process: decode1 gives
+are already resident in HBM.  Prints one JSON line (the benchmark contract) with the layer
+throughput; the roofline of the dominant kernel work, timed with HIP events on the launch
+stream over the timed region; its HBM traffic from the committed PMC summary when the kernels
+are unchanged since; and the CPU oracle timed on a bounded sample.  By default every workload below runs in turn, in one process: decode1 gives
 the line's top-level fields and the others the same fields under "legs" (decode1, decode64 and
 prefill16k share one generated expert set).  --workload runs one workload alone.
 
+Up to 128 tokens a step is one moe_layer_nvfp4 call, timed with HIP events around the timed
+steps: for one or two tokens a single persistent kernel, from three tokens the fused routing
+kernel (router, top-k, grouping, tile plan in one launch), the expert FFN and the combine; the
+roofline is then that of the whole layer.  Above 128 tokens the step is the four public calls,
+with HIP events around the expert-FFN call (its roofline) and the combine call.
+
 --combine norm replaces the plain combine with the combine variants (per-expert RMS norm before
 the weighted sum, then the residual update and the next layer's RMS norm) and runs the four-call
-path at every T; the combine call is timed with its own HIP events in both modes.
+path at every T.
 
 Workloads (hidden 7168, 256 experts, top-8, NVFP4 experts):
   decode1     T=1, expert intermediate 2048; each step takes the next token of a seeded pool of
@@ -149,8 +152,10 @@ def run_leg(wl, args, dev, shared):
 
     stream = torch.cuda.current_stream(dev)
 
-    # one or two tokens: the whole layer is one persistent kernel (plain combine only)
-    fused = T <= 2 and args.combine == "plain" and not mx8
+    # up to 128 tokens the step is one moe_layer_nvfp4 call (plain combine only): for one or two
+    # tokens a single persistent kernel, from three tokens the fused routing kernel (router,
+    # top-k, grouping, tile plan), the expert FFN and the combine
+    fused = T <= 128 and args.combine == "plain" and not mx8
     norm = args.combine == "norm"
     if norm:
         g = torch.Generator(device=dev)
@@ -239,11 +244,17 @@ def run_leg(wl, args, dev, shared):
     layer_bytes = w_bytes + T * H * 2 + H * E * 4 + T * H * 4  # weights + x + router + out
     flops = 6.0 * T * k * H * I
     traffic = None
-    if fused:
+    if fused and T <= 2:
         # the single kernel reads the expert weights, x and the router weights, writes out
         kernel, kbytes = "layer_small_kernel", layer_bytes
         if wl == "decode1":
             traffic = measured_traffic("traffic_layer_small_decode1.txt")
+    elif fused:
+        # the whole layer: expert weights, x and router weights read, out written (y and the
+        # routing arrays are intermediates)
+        kernel, kbytes = ("moe_layer_nvfp4 (route_group_kernel, expert FFN, combine)",
+                          layer_bytes)
+        traffic = measured_traffic("traffic_layer_%s.txt" % wl)
     elif mx8:
         kernel, kbytes = "fp8 expert FFN call (x quantiser + two scaled-MFMA grouped GEMMs)", ffn_bytes
         traffic = measured_traffic("traffic_ffn_mx8_%s.txt" % wl)

@@ -10,8 +10,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_nvfp4.so")
 SOURCES = ["api.hip", "route.hip", "group.hip", "ffn.hip", "combine.hip", "pack.hip", "gemm.hip",
-           "layer_small.hip", "combine_norm.hip", "mx8.hip"]
-HEADERS = [os.path.join(CSRC, "common.h"), os.path.join(CSRC, "dot.h"), os.path.join(ROOT, "include", "moe_nvfp4.h")]
+           "layer_small.hip", "combine_norm.hip", "mx8.hip", "route_group.hip"]
+HEADERS = [os.path.join(CSRC, h) for h in ("common.h", "dot.h", "sync.h", "group_dev.h", "select_dev.h")] + [
+    os.path.join(ROOT, "include", "moe_nvfp4.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

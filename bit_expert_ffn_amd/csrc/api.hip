@@ -1,7 +1,7 @@
 // C ABI of libmoe_nvfp4.so (declarations and contracts in include/moe_nvfp4.h).
 // Every entry point validates its arguments on the host before enqueueing anything; a failing
 // check returns an error code and launches nothing.
-#include "../../include/moe_nvfp4.h"
+#include "moe_nvfp4.h"
 
 #include <mutex>
 
@@ -39,7 +39,8 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   L.mx8_end = L.mx8_tiles + align_up(gemm_max_tiles(T, k, E) * sizeof(int4) + sizeof(int32_t), 256);
   L.ls_partial = base;
   L.ls_h = base + align_up((size_t)32 * T * E * sizeof(float), 256);
-  L.ls_end = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
+  L.rg_masks = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
+  L.ls_end = L.rg_masks + align_up((size_t)E * (kRgMaxT / 32) * sizeof(uint32_t), 256);
   size_t tot = L.route_end;
   if (L.group_end > tot) tot = L.group_end;
   if (L.ffn_end > tot) tot = L.ffn_end;
@@ -300,11 +301,8 @@ static moe_status layer_run(const void* x_dev, const float* w_router_dev, const 
     if (e != hipErrorInvalidConfiguration) return from_hip(e);
     // the device cannot keep one block per CU resident: run the four calls instead
   }
-  st = moe_route(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_id_dev, topk_w_dev,
-                 ws_dev, ws_bytes, stream);
-  if (st != MOE_OK) return st;
-  // the one-block grouping also writes the busy experts' tile list, which saves the FFN call's
-  // one-wavefront planning launch
+  // the grouping (fused or not) also writes the busy experts' tile list, which saves the FFN
+  // call's one-wavefront planning launch
   moe::GroupPlan gp{0, 0, 0, nullptr, nullptr};
   const bool fuse = (size_t)T * k <= (size_t)moe::kGroupSmallMax &&
                     moe::ffn_separate_plan(T, H, I, &gp.MT, &gp.min_rows);
@@ -313,9 +311,39 @@ static moe_status layer_run(const void* x_dev, const float* w_router_dev, const 
     gp.tiles = reinterpret_cast<int4*>((char*)ws_dev + L.ffn_tiles);
     gp.n_tiles = reinterpret_cast<int32_t*>(gp.tiles + gp.max_tiles);
   }
-  st = group_run(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
-                 active_dev, n_active_dev, ws_dev, ws_bytes, stream, fuse ? &gp : nullptr);
-  if (st != MOE_OK) return st;
+  bool routed = false;
+  if (moe::route_group_fits(T, k)) {
+    // router, top-k, grouping and tile list in one persistent kernel
+    moe::RouteGroupArgs r;
+    r.x = (const uint16_t*)x_dev;
+    r.wr = w_router_dev;
+    r.bias = bias_dev;
+    r.T = T; r.H = H; r.E = E; r.k = k;
+    r.logits = logits_dev;
+    r.topk_id = topk_id_dev; r.topk_w = topk_w_dev;
+    r.count = count_dev; r.offset = offset_dev; r.sorted_slot = sorted_slot_dev;
+    r.slot_row = slot_row_dev; r.active = active_dev; r.n_active = n_active_dev;
+    r.sync = reinterpret_cast<uint32_t*>(ws_dev);
+    r.partial = reinterpret_cast<float*>((char*)ws_dev + L.ls_partial);
+    r.masks = reinterpret_cast<uint32_t*>((char*)ws_dev + L.rg_masks);
+    r.plan_MT = fuse ? gp.MT : 0;
+    r.plan_min_rows = gp.min_rows;
+    r.max_tiles = gp.max_tiles;
+    r.tiles = gp.tiles;
+    r.n_tiles = gp.n_tiles;
+    const hipError_t e = moe::launch_route_group(r, (hipStream_t)stream);
+    if (e != hipSuccess && e != hipErrorInvalidConfiguration) return MOE_ERR_HIP;
+    routed = e == hipSuccess;
+    // else the device cannot keep one block per CU resident: separate kernels below
+  }
+  if (!routed) {
+    st = moe_route(x_dev, w_router_dev, bias_dev, T, H, E, k, logits_dev, topk_id_dev,
+                   topk_w_dev, ws_dev, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    st = group_run(topk_id_dev, T, k, E, count_dev, offset_dev, sorted_slot_dev, slot_row_dev,
+                   active_dev, n_active_dev, ws_dev, ws_bytes, stream, fuse ? &gp : nullptr);
+    if (st != MOE_OK) return st;
+  }
   st = expert_ffn_run(x_dev, w, count_dev, offset_dev, sorted_slot_dev, active_dev,
                       n_active_dev, T, k, y_dev, y_dtype, ws_dev, ws_bytes, stream,
                       fuse ? 1 : 0, serial);

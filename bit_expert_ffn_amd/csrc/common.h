@@ -58,6 +58,7 @@ struct WsLayout {
   size_t mx8_end;
   size_t ls_partial;     // single-launch layer: [32][T][E] fp32 router partials
   size_t ls_h;           // single-launch layer: [T*k][I] f16
+  size_t rg_masks;       // fused routing: [E][4] token masks
   size_t ls_end;
   size_t total;
 };
@@ -138,6 +139,29 @@ struct LayerSmallArgs {
 size_t layer_small_lds(int T, int H, int I, int k);
 bool layer_small_fits(int T, int H, int I, int E, int k);
 hipError_t launch_layer_small(const LayerSmallArgs& a, hipStream_t s);
+
+// Fused routing for a small batch (route_group.hip): router, top-k + softmax, grouping and the
+// grouped GEMM's tile plan in one persistent kernel, for T <= kRgMaxT and T * k <= kRgMaxSlots.
+constexpr int kRgMaxT = 128;
+constexpr int kRgMaxSlots = 4096;
+struct RouteGroupArgs {
+  const uint16_t* x;  // [T][H] bf16
+  const float* wr;    // [H][E]
+  const float* bias;  // [E] or null
+  int T, H, E, k;
+  float* logits;  // [T][E] or null
+  int32_t* topk_id;
+  float* topk_w;
+  int32_t *count, *offset, *sorted_slot, *slot_row, *active, *n_active;
+  uint32_t* sync;   // kSyncBytes: counters and flags (shared with the single-launch layer)
+  float* partial;   // [32][T][E]
+  uint32_t* masks;  // [E][kRgMaxT / 32] token masks
+  int plan_MT, plan_min_rows, max_tiles;  // plan_MT == 0: no tile list
+  int4* tiles;
+  int32_t* n_tiles;
+};
+bool route_group_fits(int T, int k);
+hipError_t launch_route_group(const RouteGroupArgs& a, hipStream_t s);
 
 hipError_t launch_pack(const uint8_t* q_in, const uint8_t* s_in, int E, int N, int K,
                        uint8_t* q_out, uint8_t* s_out, hipStream_t s);

@@ -43,6 +43,8 @@
 
 #include "common.h"
 #include "dot.h"
+#include "select_dev.h"
+#include "sync.h"
 
 namespace moe {
 
@@ -50,84 +52,6 @@ constexpr int kLsNS = 32;                 // router: slices of the hidden dimens
 constexpr int kLsEG = 32;                 // router: experts per item
 constexpr int kLsSetC = 4;                // gate/up: chunks per load set
 constexpr int kLsSetD = 8;                // down: chunks per load set
-constexpr uint32_t kLsSpin = 1u << 21;    // default polls before a wait gives up (about 2 s)
-// Sync region (kSyncBytes at the start of the workspace), in 32-bit words: arrival counters A,
-// C, X and the error word, 64 bytes apart, the spin-limit word right after the error word;
-// then kLsFlags copies of the "all arrived" flags of barriers A and C, 4 KB apart so that the
-// pollers of different copies hit different memory channels.
-constexpr int kLsSyncA = 0, kLsSyncC = 16, kLsSyncX = 32, kLsSyncErr = kSyncErrWord;
-constexpr int kLsSyncSpin = kSyncSpinWord;
-constexpr int kLsFlags = 16, kLsFlagBase = 64, kLsFlagStride = 1024;
-constexpr int kLsFlagA = 0, kLsFlagC = 16;
-static_assert((kLsFlagBase + (kLsFlags - 1) * kLsFlagStride + kLsFlagC + 1) * 4 <= kSyncBytes,
-              "flags must fit in the sync region");
-
-__device__ inline uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Every earlier store of this block is complete, then thread 0 adds one to the counter; the
-// block that brings it to G raises every copy of the barrier's flag.
-__device__ inline void ls_arrive(uint32_t* sync, int ctr, int flag, uint32_t G) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  lds_barrier();
-  if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(sync + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1)
-      for (int i = 0; i < kLsFlags; ++i) st_dev(sync + kLsFlagBase + i * kLsFlagStride + flag, 1u);
-  }
-}
-
-// Thread 0 polls this block's copy of the flag; the other wavefronts wait at an LDS-only
-// barrier, keeping their own loads in flight.  false (for every thread) after `limit` polls.
-__device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t limit) {
-  if (threadIdx.x == 0) {
-    const uint32_t* f = sync + kLsFlagBase + (blockIdx.x % kLsFlags) * kLsFlagStride + flag;
-    uint32_t spins = 0;
-    int ok = 1;
-    while (ld_dev(f) == 0) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > limit) {
-        ok = 0;
-        __hip_atomic_fetch_or(sync + kLsSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    *s_ok = ok;
-  }
-  lds_barrier();
-  const bool ok = *s_ok != 0;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return ok;
-}
-
-// Exit, for a block that finished its work or gave up waiting: once this block's stores are
-// complete, thread 0 arrives at counter X; the last block to arrive (every block has then
-// stopped polling) resets the counters and flags for the next call.  The error word and the
-// spin-limit word are left as they are.
-__device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // this block's flag stores are complete
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const uint32_t old =
-        __hip_atomic_fetch_add(sync + kLsSyncX, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1) {
-      st_dev(sync + kLsSyncA, 0u);
-      st_dev(sync + kLsSyncC, 0u);
-      for (int i = 0; i < kLsFlags; ++i) {
-        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
-        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
-      }
-      st_dev(sync + kLsSyncX, 0u);
-    }
-  }
-}
-
 // A block that gave up waiting writes NaN over its output tiles (the 32-feature tiles
 // blockIdx.x + m * G of every token), so a failed call shows in out: a give-up at barrier A
 // keeps barrier A or C from completing for everyone, so every block with output tiles gives up.
@@ -140,21 +64,6 @@ __device__ inline void ls_fail_out(const LayerSmallArgs& a, int G) {
 
 // Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
 extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
-
-// Selection key of a logit: larger key = larger logit, equal logits -> the lower expert id.  -0
-// counts as +0 and NaN as -inf.  0 is below every key (an empty candidate).
-__device__ inline uint64_t sel_key(float v, int id) {
-  v = v == v ? v + 0.0f : -__builtin_inff();
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
-}
-__device__ inline float sel_value(uint64_t key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-  return __uint_as_float(u);
-}
-__device__ inline int sel_id(uint64_t key) { return (int)~(uint32_t)key; }
 
 // Orders the LDS accesses of one wavefront (its lanes read what other lanes just wrote).
 __device__ inline void wave_lds_sync() {

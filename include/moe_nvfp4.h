@@ -237,11 +237,19 @@ moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *s
  * That path writes logits (if not NULL), topk_id, topk_w, the grouping arrays and out, but not
  * y; the combine there adds each token's experts in the order of the active list rather than
  * by slot.
- * Larger T, or a device that cannot keep one block per CU resident, run the four calls in
- * order, y_dev ([T*k][H] of y_dtype, grouped row order) holding the expert outputs.  There
- * the one-block grouping also writes the grouped GEMM's tile list into ws_dev, which saves
- * the expert-FFN call one launch; every output is bit-identical to that of the four calls.
- * Calls that share ws_dev must not overlap in time. */
+ * From 3 to 128 tokens (T*k <= 4096) the router, top-k + softmax, grouping and the grouped
+ * GEMM's tile list run as ONE persistent kernel (same pages and sections), then the expert FFN
+ * and the combine: y_dev ([T*k][H] of y_dtype, grouped row order) holds the expert outputs.
+ * Its logits are summed on the matrix cores from exact three-piece bf16 splits of the fp32
+ * router weights, so they differ from moe_route's only in the order of fp32 additions; ids,
+ * weights and grouping follow from the logits exactly as in moe_route and moe_group.  It
+ * waits at grid barriers like the single-launch kernel (same precondition and error word; if a
+ * wait gives up, the grouping arrays describe no active expert and topk_w is NaN, so the
+ * later kernels do nothing and out shows NaN).
+ * Above 128 tokens, or on a device that cannot keep one block per CU resident, the four calls
+ * run in order, and the one-block grouping also writes the grouped GEMM's tile list into
+ * ws_dev, which saves the expert-FFN call one launch; every output is then bit-identical to
+ * that of the four calls.  Calls that share ws_dev must not overlap in time. */
 moe_status moe_layer_nvfp4(const void *x_dev, const float *w_router_dev, const float *bias_dev,
                            const moe_nvfp4_experts *w, int32_t T, int32_t k, float *logits_dev,
                            int32_t *topk_id_dev, float *topk_w_dev, int32_t *count_dev,

@@ -122,6 +122,10 @@ def test_decode64_full():
     _check_tokens(sp, L, ex_host, buf, list(range(sp["T"])), L["x"])
 
 
+def test_decode64_layer_entry():
+    _entry_against_four_calls("decode64", [0, 13, 31, 50, 63])
+
+
 def test_verify128_full():
     """Every one of the 128 tokens against the oracle (Zipf-skewed loads: busy experts on
     several 32-row GEMM tiles)."""
@@ -132,6 +136,51 @@ def test_verify128_full():
     counts = buf.count.cpu().numpy()
     assert counts.max() > 32  # the Zipf bias gives some experts several 32-row tiles
     _check_tokens(sp, L, ex_host, buf, list(range(sp["T"])), L["x"])
+
+
+def _run_entry(L, x, k):
+    """moe_layer_nvfp4 (for 3..128 tokens: the fused routing kernel, then the expert FFN and
+    the combine), as the benchmark times the layer at these sizes."""
+    import bit_expert_ffn_amd as moe
+    T, H = x.shape
+    ex = L.setdefault("_packed", None) or moe.pack_experts(L["experts"])
+    L["_packed"] = ex
+    E, I = ex["gate_q"].shape[0], ex["gate_q"].shape[1]
+    buf = moe.LayerBuffers(T, H, I, E, k, device="cuda", y_dtype=torch.float16)
+    moe.layer_nvfp4(x, L["w_router"], L["bias"], ex, k, buf)
+    torch.cuda.synchronize()
+    moe.layer_check(buf.ws)
+    return buf
+
+
+def _entry_against_four_calls(name, sample):
+    """The layer entry against the four public calls (checked against the oracle on every
+    token above) on every token, and against the oracle directly on a sample of tokens."""
+    from parity import route_candidates
+    sp, L, ex_host = _layer(name)
+    k = sp["k"]
+    print("case %s through moe_layer_nvfp4" % name, flush=True)
+    be = _run_entry(L, L["x"], k)
+    b4 = _run(L, L["x"], k)
+    _check_group_invariants(be, sp["E"], k)
+    ge, g4 = be.topk_id.cpu().numpy(), b4.topk_id.cpu().numpy()
+    diff = np.nonzero((ge != g4).any(1))[0]
+    if len(diff):
+        xb = L["x"].cpu().view(torch.int16).numpy().view(np.uint16)
+        wr = L["w_router"].cpu().numpy()
+        bias = None if L["bias"] is None else L["bias"].cpu().numpy()
+        lg = oracle.router(xb[diff], wr, bias)
+        for i, t in enumerate(diff):
+            c = route_candidates(lg[i], k)
+            assert tuple(ge[t]) in c and tuple(g4[t]) in c, "token %d: not a near-tie" % t
+    same = np.setdiff1d(np.arange(sp["T"]), diff)
+    check_out(be.out.cpu().numpy()[same], b4.out.cpu().numpy()[same].astype(np.float64),
+              max_rel=1e-4, mae=1e-5)
+    _check_tokens(sp, L, ex_host, be, sample, L["x"])
+
+
+def test_verify128_layer_entry():
+    _entry_against_four_calls("verify128", list(range(0, 128, 9)))
 
 
 def tile_covering_tokens(buf, k, mt=128, n=128):
