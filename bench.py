@@ -14,6 +14,10 @@ kernel (router, top-k, grouping, tile plan in one launch), the expert FFN and th
 roofline is then that of the whole layer.  Above 128 tokens the step is the four public calls,
 with HIP events around the expert-FFN call (its roofline) and the combine call.
 
+Warmup: the W warmup steps, then untimed steps until --settle-s seconds (default 0.3) of warmup
+have passed: a GPU that was idle runs its first milliseconds of work at lower clocks, and a few
+steps of a short workload do not cover that ramp.  The JSON line reports both counts.
+
 --combine norm replaces the plain combine with the combine variants (per-expert RMS norm before
 the weighted sum, then the residual update and the next layer's RMS norm) and runs the four-call
 path at every T.
@@ -72,6 +76,10 @@ def main():
     ap.add_argument("--precision", default="nvfp4", choices=["nvfp4", "mx8"],
                     help="mx8: the fp8-compute variant (MXFP8 weights requantised from NVFP4 at "
                          "load time, MXFP8 x and h, scaled matrix cores; four-call path)")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="after the W warmup steps, keep running untimed steps until this many "
+                         "seconds of warmup have passed, so the timed steps run at the clocks of "
+                         "a busy GPU, not those of one that was idle (0 disables)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget per workload (0 disables the CPU baseline)")
     args = ap.parse_args()
@@ -99,7 +107,7 @@ def main():
 
 def leg_summary(r):
     """The per-workload record under 'legs' of the headline line."""
-    keep = ("value", "unit", "steps", "warmup", "ms_per_step", "us_per_layer", "kernel_us",
+    keep = ("value", "unit", "steps", "warmup", "settle_steps", "ms_per_step", "us_per_layer", "kernel_us",
             "dtype", "config", "roofline", "cpu_baseline", "distinct_experts", "layer_hbm_frac",
             "kernel_algorithmic_bytes", "combine", "ffn_flops")
     return {k: r[k] for k in keep if k in r}
@@ -199,10 +207,21 @@ def run_leg(wl, args, dev, shared):
         if evc is not None:
             evc[1].record(stream)
 
+    t_w = time.perf_counter()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    print("%s: warmup done; timing %d steps" % (wl, steps), file=sys.stderr, flush=True)
+    # settle: a GPU that was idle (host-side setup, another workload's CPU baseline) runs its
+    # first milliseconds of work at lower clocks; a few warmup steps of a short workload do not
+    # cover that ramp, so untimed steps continue until settle_s seconds of warmup have passed
+    settle = 0
+    while time.perf_counter() - t_w < args.settle_s:
+        for _ in range(8):
+            step(warmup + settle)
+            settle += 1
+        torch.cuda.synchronize()
+    print("%s: warmup done (%d steps + %d settle steps); timing %d steps" % (
+        wl, warmup, settle, steps), file=sys.stderr, flush=True)
 
     # timed region: exactly `steps` layer calls, bracketed by device synchronisation
     # HIP events on the launch stream: around the expert-FFN call of every step (four-call
@@ -296,7 +315,8 @@ def run_leg(wl, args, dev, shared):
 
     return {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "steps": steps, "warmup": warmup, "settle_steps": settle, "settle_s": args.settle_s,
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8 (e4m3, MX)" if mx8 else "f16",
         "data": "synthetic",
