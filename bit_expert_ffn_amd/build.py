@@ -9,6 +9,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_nvfp4.so")
+# profiling build: the persistent kernels record per-block phase timestamps (-DMOE_TIMELINE)
+TIMELINE_BUILD = os.path.join(PKG, "_build_timeline")
+TIMELINE_LIB = os.path.join(PKG, "libmoe_nvfp4_timeline.so")
 SOURCES = ["api.hip", "route.hip", "group.hip", "ffn.hip", "combine.hip", "pack.hip", "gemm.hip",
            "layer_small.hip", "combine_norm.hip", "mx8.hip", "route_group.hip"]
 HEADERS = [os.path.join(CSRC, h) for h in ("common.h", "dot.h", "sync.h", "group_dev.h", "select_dev.h")] + [
@@ -23,30 +26,33 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose=True):
-    """Compile every HIP source (always, also when a library exists) and link the library."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=True, timeline=False):
+    """Compile every HIP source (always, also when a library exists) and link the library.
+    timeline=True builds the profiling library (libmoe_nvfp4_timeline.so, -DMOE_TIMELINE)."""
+    bdir, lib = (TIMELINE_BUILD, TIMELINE_LIB) if timeline else (BUILD, LIB)
+    extra = ("-DMOE_TIMELINE",) if timeline else ()
+    os.makedirs(bdir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, bdir, extra), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB, file=sys.stderr)
-    return LIB
+        print("built", lib, file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv[1:])

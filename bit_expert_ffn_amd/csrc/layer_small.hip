@@ -50,6 +50,23 @@
 
 namespace moe {
 
+// Profiling builds only (compiled with -DMOE_TIMELINE): each block's first thread records the
+// 100 MHz real-time counter at the phase boundaries of the last call, read back with
+// moe_timeline_layer_small.  Slots: 0 entry, 1 router partials stored, 2 barrier A passed,
+// 3 first gate/up weights requested, 4 gate/up done, 5 barrier C passed, 6 h staged, 7 exit.
+#ifdef MOE_TIMELINE
+__device__ unsigned long long g_ls_timeline[1024][8];
+#define LS_STAMP(i)                                                                 \
+  do {                                                                              \
+    if (threadIdx.x == 0 && blockIdx.x < 1024)                                      \
+      g_ls_timeline[blockIdx.x][i] = __builtin_amdgcn_s_memrealtime();              \
+  } while (0)
+#else
+#define LS_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
+
 constexpr int kLsNS = 32;                 // router: slices of the hidden dimension
 constexpr int kLsEG = 32;                 // router: experts per item
 constexpr int kLsSetC = 4;                // gate/up: chunks per load set
@@ -90,6 +107,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   __shared__ float dred[4][TT][16];
   __shared__ int s_nact, s_flag;
 
+  LS_STAMP(0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int G = gridDim.x;
@@ -157,6 +175,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       __syncthreads();
     }
   }
+  LS_STAMP(1);
   ls_arrive(a.sync, kLsSyncA, kLsFlagA, (uint32_t)G);
   // x rows into LDS for the gate/up phase, while barrier A completes
   for (int i = tid; i < T * H / 8; i += 256)
@@ -226,6 +245,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     ls_exit(a.sync, (uint32_t)G);
     return;
   }
+  LS_STAMP(2);
   // logits of expert e = tid (slices added in order), kept in registers
   float lg[TT];
 #pragma unroll
@@ -455,6 +475,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     }
   }
 
+  LS_STAMP(3);
   // ---- C: gate/up + SwiGLU; rows of h (f16) go out with device-scope stores ----
   {
     float ag[TT], au[TT];
@@ -525,6 +546,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       }
     }
   }
+  LS_STAMP(4);
   ls_arrive(a.sync, kLsSyncC, kLsFlagC, (uint32_t)G);
 
   // ---- D: down + combine ----
@@ -565,6 +587,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         ls_exit(a.sync, (uint32_t)G);
         return;
       }
+      LS_STAMP(5);
       if (has_k && wv == 0) load_set(qA, sA, 0);
       // both halves of every h row: LDS [half][row][hw_row words], read with device-scope
       // 64-bit loads (the rows were written by other blocks)
@@ -581,6 +604,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
             make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
       }
       lds_barrier();
+      LS_STAMP(6);
     }
     const uint32_t* hs = dyn;
     for (; ftp < npairs; ftp += G) {
@@ -647,6 +671,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   }
 
   // ---- exit: the last block resets the counters and flags for the next call ----
+  LS_STAMP(7);
   ls_exit(a.sync, (uint32_t)G);
 }
 
@@ -716,3 +741,9 @@ hipError_t launch_layer_small(const LayerSmallArgs& a, hipStream_t s) {
 
 }  // namespace moe
 
+#ifdef MOE_TIMELINE
+extern "C" __attribute__((visibility("default"))) int moe_timeline_layer_small(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::g_ls_timeline), sizeof(moe::g_ls_timeline),
+                                  0, hipMemcpyDeviceToHost);
+}
+#endif

@@ -45,6 +45,24 @@
 
 namespace moe {
 
+// Profiling builds only (compiled with -DMOE_TIMELINE): each block's first thread records the
+// 100 MHz real-time counter at the phase boundaries of the last call, read back with
+// moe_timeline_route_group.  Slots: 0 entry, 1 router partials stored, 2 barrier A passed (token
+// blocks), 3 top-k done, 4 barrier C passed, 5 rows placed, 6 block 0: active list sorted,
+// 7 exit.
+#ifdef MOE_TIMELINE
+__device__ unsigned long long g_rg_timeline[1024][8];
+#define RG_STAMP(i)                                                                 \
+  do {                                                                              \
+    if (threadIdx.x == 0 && blockIdx.x < 1024)                                      \
+      g_rg_timeline[blockIdx.x][i] = __builtin_amdgcn_s_memrealtime();              \
+  } while (0)
+#else
+#define RG_STAMP(i) \
+  do {              \
+  } while (0)
+#endif
+
 constexpr int kRgSlices = 32;  // phase A: slices of the hidden dimension
 constexpr int kRgEG = 32;      // phase A: experts per item
 constexpr int kRgBatch = 4;    // phase A: steps per wavefront whose loads are in flight together
@@ -125,6 +143,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
   __shared__ int off[kMaxExperts + 4];
   __shared__ int act_l[kMaxExperts];
 
+  RG_STAMP(0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x;
   const int T = a.T, H = a.H, E = a.E, k = a.k;
@@ -206,6 +225,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
       __syncthreads();
     }
   }
+  RG_STAMP(1);
   ls_arrive(a.sync, kLsSyncA, kLsFlagA, (uint32_t)G);
 
   // ---- B: one token per block: logits, top-k, softmax ----
@@ -216,6 +236,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
       ls_exit(a.sync, (uint32_t)G);
       return;
     }
+    RG_STAMP(2);
     float lg = 0.f;
     uint64_t key = 0;  // below every real key
     if (tid < E) {
@@ -257,6 +278,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  RG_STAMP(3);
   ls_arrive(a.sync, kLsSyncC, kLsFlagC, (uint32_t)G);
 
   // ---- C: every token block places its own k rows; block 0 also writes the per-expert
@@ -269,6 +291,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
       ls_exit(a.sync, (uint32_t)G);
       return;
     }
+    RG_STAMP(4);
     const int mw = (T + 31) >> 5;  // mask words in use
     int c = 0;
     if (tid < E) {
@@ -293,6 +316,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
       a.slot_row[slot] = pos;
       a.sorted_slot[pos] = slot;
     }
+    RG_STAMP(5);
     if (blockIdx.x == 0) {
       if (tid < E) {
         a.count[tid] = cnt[tid];
@@ -312,11 +336,13 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
         s_nact = nact;
       }
       __syncthreads();
+      RG_STAMP(6);
       if (a.plan_MT > 0 && wv == 0)
         ffn_plan_n(cnt, off, act_l, s_nact, a.plan_MT, a.plan_min_rows, a.tiles, a.max_tiles,
                    a.n_tiles);
     }
   }
+  RG_STAMP(7);
   ls_exit(a.sync, (uint32_t)G);
 }
 
@@ -367,3 +393,10 @@ hipError_t launch_route_group(const RouteGroupArgs& a, hipStream_t s) {
 }
 
 }  // namespace moe
+
+#ifdef MOE_TIMELINE
+extern "C" __attribute__((visibility("default"))) int moe_timeline_route_group(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::g_rg_timeline), sizeof(moe::g_rg_timeline),
+                                  0, hipMemcpyDeviceToHost);
+}
+#endif
