@@ -53,9 +53,11 @@ namespace moe {
 // Profiling builds only (compiled with -DMOE_TIMELINE): each block's first thread records the
 // 100 MHz real-time counter at the phase boundaries of the last call, read back with
 // moe_timeline_layer_small.  Slots: 0 entry, 1 router partials stored, 2 barrier A passed,
-// 3 first gate/up weights requested, 4 gate/up done, 5 barrier C passed, 6 h staged, 7 exit.
+// 3 routing published (gate/up starts), 4 gate/up done, 5 barrier C passed, 6 h staged, 7 exit;
+// inside the routing: 8 logits summed, 9 first-level ranks, 10 candidate ranks, 11 first gate/up
+// sets issued (one token).
 #ifdef MOE_TIMELINE
-__device__ unsigned long long g_ls_timeline[1024][8];
+__device__ unsigned long long g_ls_timeline[1024][16];
 #define LS_STAMP(i)                                                                 \
   do {                                                                              \
     if (threadIdx.x == 0 && blockIdx.x < 1024)                                      \
@@ -264,6 +266,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       lg[t] = sum;
     }
   }
+  LS_STAMP(8);
   // top-k in two levels, by rank: an expert's rank is the number of experts with a larger
   // selection key (a larger logit, or an equal logit and a lower id).  Each lane first ranks
   // its expert among the 64 of its wavefront; those of rank < k are the candidates (the overall
@@ -288,6 +291,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     wave_lds_sync();
   }
   lds_barrier();
+  LS_STAMP(9);
   // candidate keys (two per lane) and their ranks among the candidates
   uint64_t cc0[TT], cc1[TT];
   int rr0[TT], rr1[TT];
@@ -307,6 +311,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     rr0[t] = r0;
     rr1[t] = r1;
   }
+  LS_STAMP(10);
   if constexpr (TT == 1) {
     // the first two gate/up load sets are requested now: the expert of slot r is the candidate
     // of rank r
@@ -323,6 +328,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       load_set(qgB, quB, sgB, suB, lc, slot_expert(lc.ai));
       cur_next(lc);
     }
+    LS_STAMP(11);
   }
   // each token's slots into lanes (lane r < k: slot r), through this wavefront's LDS
   uint64_t sk[TT];

@@ -24,8 +24,10 @@ import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-LAYER_SMALL = ["entry", "router partials stored", "barrier A passed", "first gate/up weights requested",
-               "gate/up done", "barrier C passed", "h staged", "exit"]
+LAYER_SMALL = ["entry", "router partials stored", "barrier A passed", "routing published, gate/up starts",
+               "gate/up done", "barrier C passed", "h staged", "exit", "logits summed", "first-level ranks",
+               "candidate ranks (top-k known)", "first gate/up sets issued"]
+LAYER_SMALL_ORDER = [0, 1, 2, 8, 9, 10, 11, 3, 4, 5, 6, 7]
 ROUTE_GROUP = ["entry", "router partials stored", "barrier A passed", "top-k done", "barrier C passed",
                "rows placed", "active list sorted", "exit"]
 # blocks that record each slot of the fused routing kernel: all, or the T token blocks, or block 0
@@ -36,6 +38,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("workload")
     ap.add_argument("--calls", type=int, default=50)
+    ap.add_argument("--per-block", type=int, default=None, metavar="SLOT",
+                    help="also print each block's median time at this slot (blocks go round-robin "
+                         "to the 8 XCDs, so block b runs on XCD b %% 8), and the per-XCD medians")
     args = ap.parse_args()
     import bit_expert_ffn_amd as moe
     from bit_expert_ffn_amd import build as b
@@ -78,7 +83,7 @@ def main():
             calls[i % pool]()
             i += 1
         torch.cuda.synchronize()
-        h = np.zeros((1024, 8), np.uint64)
+        h = np.zeros((1024, 16 if small else 8), np.uint64)
         if read(ctypes.c_void_p(h.ctypes.data)) != 0:
             sys.exit("reading the timeline failed")
         runs.append(h)
@@ -94,7 +99,8 @@ def main():
     rel = np.stack(rel)  # [calls][blocks][slots]
     print("%s: %s, T=%d, %d blocks, %d calls (us from the first block's entry)" % (
         "layer_small_kernel" if small else "route_group_kernel", args.workload, T, G, args.calls))
-    for j, name in enumerate(names):
+    for j in (LAYER_SMALL_ORDER if small else range(len(names))):
+        name = names[j]
         who = "all" if small else ROUTE_GROUP_BLOCKS[j]
         v = rel[:, :T, j] if who == "token" else rel[:, :1, j] if who == "block 0" else rel[:, :, j]
         v = v[~np.isnan(v)]
@@ -103,6 +109,15 @@ def main():
                                                     "block 0" if who == "block 0" else "all blocks")
             print("  %-44s median %7.2f   p90 %7.2f   max %7.2f" % (
                 label, np.median(v), np.percentile(v, 90), v.max()))
+    if args.per_block is not None:
+        med = np.nanmedian(rel[:, :, args.per_block], axis=0)  # [blocks]
+        print("slot %d (%s), median over calls per block:" % (args.per_block, names[args.per_block]))
+        for x in range(8):
+            v = med[x::8]
+            v = v[~np.isnan(v)]
+            print("  XCD %d (blocks %d, %d, ...): median %7.2f  max %7.2f" % (x, x, x + 8, np.median(v), v.max()))
+        order = np.argsort(-np.nan_to_num(med, nan=-1.0))[:16]
+        print("  latest blocks: " + ", ".join("%d (%.2f)" % (b, med[b]) for b in order))
 
 
 if __name__ == "__main__":
