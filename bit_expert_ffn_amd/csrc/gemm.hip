@@ -80,8 +80,10 @@ __global__ __launch_bounds__(64) void ffn_plan_kernel(
 // K may be permuted: step i takes codes 8i..8i+7 of the lane's group, and the activation
 // operand is read from LDS columns 32 (l / 32) + 8i of the stage (same permutation).  Global
 // loads of activations and packed weights run ahead in S register sets.
+// The launch bound's second argument is the minimum number of wavefronts per SIMD: two (up to
+// 256 VGPRs) below 8 wavefronts per block, one with 8 (whose 512 threads give two per SIMD).
 template <bool GATEUP, int MTT, bool Y_F16, int S, int NW, bool XBF>
-__global__ __launch_bounds__(64 * NW, 512 / (64 * NW)) void ffn_gemm_kernel(
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void ffn_gemm_kernel(
     const uint16_t* __restrict__ xa, const uint8_t* __restrict__ qm0,
     const uint8_t* __restrict__ sm0, const uint8_t* __restrict__ qm1,
     const uint8_t* __restrict__ sm1, const float* __restrict__ ts,
@@ -355,10 +357,13 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
   // 128-row tiles from 2048 tokens: 8 wavefronts (512 weight rows per block); 64-row tiles from
   // 512 tokens and 32-row tiles below, on 4 wavefronts: most experts of a small batch have a
   // few rows, and a smaller tile wastes fewer matrix-core cycles on rows past the expert's end
-  // (measured at T = 128: 130 against 153 us; at T = 64: 954 against 965 us)
+  // (measured at T = 128: 130 against 153 us; at T = 64: 954 against 965 us).  The gate/up of
+  // narrow experts (I <= 512, six register sets) takes 2-wavefront blocks: twice the blocks, so
+  // that more CUs hold two of them (measured at T = 128, I = 256: expert FFN 117.5 against
+  // 119.3 us)
 #define MOE_GEMM(GU_, MT_, S_, F16_, XBF_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                       \
   do {                                                                                        \
-    constexpr int NW_ = MT_ == 128 ? 8 : 4;                                                   \
+    constexpr int NW_ = MT_ == 128 ? 8 : (GU_ && MT_ == 32 && S_ == 6) ? 2 : 4;              \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
     ffn_gemm_kernel<GU_, MT_, F16_, S_, NW_, XBF_><<<g_, 64 * NW_, 0, s>>>(                   \
