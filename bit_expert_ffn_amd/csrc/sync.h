@@ -1,15 +1,20 @@
 // Grid-wide barriers of the persistent kernels (one block per CU, every block resident): the
 // single-launch layer and the fused routing kernel.  Internal header.
 //
-// The sync region is the first kSyncBytes of the workspace, in 32-bit words: arrival counters
-// A, C and X and the error word, 64 bytes apart, the spin-limit word right after the error
-// word; then kLsFlags copies of the "all arrived" flags of barriers A and C, 4 KB apart so that
-// the pollers of different copies hit different memory channels.  A barrier: every block adds
-// one to the barrier's counter (a relaxed device-scope atomic, issued after a full s_waitcnt so
-// that this block's earlier device-scope stores are complete); the block that completes it
-// raises every copy of the flag; each block polls its own copy.  Every wait is bounded.  At the
-// exit every block adds one to counter X, and the last one resets the counters and flags: every
-// call leaves them zero, whether or not its waits gave up.
+// The sync region is the first kSyncBytes of the workspace, in 32-bit words: the top-level
+// arrival counters of barriers A, C and X and the error word, 64 bytes apart, the spin-limit
+// word right after the error word; then kLsFlags copies of the "all arrived" flags of barriers
+// A and C, 4 KB apart so that the pollers of different copies hit different memory channels;
+// then the group counters, one 128-byte line each.  A barrier has two levels: every block adds
+// one to the counter of its group (blocks b with the same b % 8, which the hardware places on
+// one XCD), and the last arrival of each group adds one to the barrier's top-level counter; the
+// block that completes that raises every copy of the flag, and each block polls its own copy.
+// (Arrivals at one counter are serialised where the atomics execute: 256 of them on one word
+// cost about 3 us, 32 on each of 8 words plus 8 on the top about a third of that.)  Every atomic
+// is a relaxed device-scope one, issued after a full s_waitcnt so that the block's earlier
+// device-scope stores are complete.  Every wait is bounded.  At the exit every block arrives
+// at barrier X the same way, and the block that completes it resets every counter and flag:
+// every call leaves them zero, whether or not its waits gave up.
 #pragma once
 #include "common.h"
 
@@ -20,8 +25,12 @@ constexpr int kLsSyncA = 0, kLsSyncC = 16, kLsSyncX = 32, kLsSyncErr = kSyncErrW
 constexpr int kLsSyncSpin = kSyncSpinWord;
 constexpr int kLsFlags = 16, kLsFlagBase = 64, kLsFlagStride = 1024;
 constexpr int kLsFlagA = 0, kLsFlagC = 16;
-static_assert((kLsFlagBase + (kLsFlags - 1) * kLsFlagStride + kLsFlagC + 1) * 4 <= kSyncBytes,
-              "flags must fit in the sync region");
+constexpr int kLsGroups = 8;           // arrival groups: blocks with the same index mod 8
+constexpr int kLsGroupBase = 15488;    // group counters: word kLsGroupBase + 32 (3 g + barrier)
+static_assert((kLsFlagBase + (kLsFlags - 1) * kLsFlagStride + kLsFlagC + 1) < kLsGroupBase,
+              "flags end before the group counters");
+static_assert((kLsGroupBase + 32 * 3 * kLsGroups) * 4 <= kSyncBytes,
+              "group counters must fit in the sync region");
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -30,16 +39,32 @@ __device__ inline void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every earlier store of this block is complete, then thread 0 adds one to the counter; the
-// block that brings it to G raises every copy of the barrier's flag.
+// The group counter of barrier `bar` (0: A, 1: C, 2: X) for group g.
+__device__ inline uint32_t* ls_group_ctr(uint32_t* sync, int bar, int g) {
+  return sync + kLsGroupBase + 32 * (3 * g + bar);
+}
+
+// Thread 0 only: this block's arrival at barrier `bar` (top-level counter word `top`) of a grid
+// of G blocks; true for the one block whose arrival completes it.
+__device__ inline bool ls_count(uint32_t* sync, int bar, int top, uint32_t G) {
+  const uint32_t g = blockIdx.x % kLsGroups;
+  const uint32_t gsize = G / kLsGroups + (g < G % kLsGroups ? 1u : 0u);
+  const uint32_t old = __hip_atomic_fetch_add(ls_group_ctr(sync, bar, (int)g), 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  if (old != gsize - 1) return false;
+  const uint32_t ngroups = G < (uint32_t)kLsGroups ? G : (uint32_t)kLsGroups;
+  return __hip_atomic_fetch_add(sync + top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+         ngroups - 1;
+}
+
+// Every earlier store of this block is complete, then thread 0 arrives; the block whose
+// arrival completes the barrier raises every copy of its flag.
 __device__ inline void ls_arrive(uint32_t* sync, int ctr, int flag, uint32_t G) {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   lds_barrier();
   if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(sync + ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1)
+    if (ls_count(sync, ctr == kLsSyncA ? 0 : 1, ctr, G))
       for (int i = 0; i < kLsFlags; ++i) st_dev(sync + kLsFlagBase + i * kLsFlagStride + flag, 1u);
   }
 }
@@ -68,18 +93,18 @@ __device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t lim
 }
 
 // Exit, for a block that finished its work or gave up waiting: once this block's stores are
-// complete, thread 0 arrives at counter X; the last block to arrive (every block has then
-// stopped polling) resets the counters and flags for the next call.  The error word and the
+// complete, thread 0 arrives at barrier X; the block that completes it (every block has then
+// stopped polling) resets every counter and flag for the next call.  The error word and the
 // spin-limit word are left as they are.
 __device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
   if (threadIdx.x == 0) {
     __builtin_amdgcn_s_waitcnt(0);  // this block's flag stores are complete
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const uint32_t old =
-        __hip_atomic_fetch_add(sync + kLsSyncX, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == G - 1) {
+    if (ls_count(sync, 2, kLsSyncX, G)) {
       st_dev(sync + kLsSyncA, 0u);
       st_dev(sync + kLsSyncC, 0u);
+      for (int g = 0; g < kLsGroups; ++g)
+        for (int bar = 0; bar < 3; ++bar) st_dev(ls_group_ctr(sync, bar, g), 0u);
       for (int i = 0; i < kLsFlags; ++i) {
         st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
         st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
