@@ -40,7 +40,8 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   L.ls_partial = base;
   L.ls_h = base + align_up((size_t)32 * T * E * sizeof(float), 256);
   L.rg_masks = L.ls_h + align_up(n * I * sizeof(_Float16), 256);
-  L.ls_end = L.rg_masks + align_up((size_t)E * (kRgMaxT / 32) * sizeof(uint32_t), 256);
+  L.ls_xpart = L.rg_masks + align_up((size_t)E * (kRgMaxT / 32) * sizeof(uint32_t), 256);
+  L.ls_end = L.ls_xpart + align_up((size_t)k * H * sizeof(float), 256);
   size_t tot = L.route_end;
   if (L.group_end > tot) tot = L.group_end;
   if (L.ffn_end > tot) tot = L.ffn_end;
@@ -297,6 +298,7 @@ static moe_status layer_run(const void* x_dev, const float* w_router_dev, const 
     a.sync = reinterpret_cast<uint32_t*>(ws_dev);
     a.partial = reinterpret_cast<float*>((char*)ws_dev + L.ls_partial);
     a.h = reinterpret_cast<uint32_t*>((char*)ws_dev + L.ls_h);
+    a.xpart = reinterpret_cast<float*>((char*)ws_dev + L.ls_xpart);
     const hipError_t e = moe::launch_layer_small(a, (hipStream_t)stream);
     if (e != hipErrorInvalidConfiguration) return from_hip(e);
     // the device cannot keep one block per CU resident: run the four calls instead

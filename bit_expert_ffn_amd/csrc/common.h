@@ -59,6 +59,7 @@ struct WsLayout {
   size_t ls_partial;     // single-launch layer: [32][T][E] fp32 router partials
   size_t ls_h;           // single-launch layer: [T*k][I] f16
   size_t rg_masks;       // fused routing: [E][4] token masks
+  size_t ls_xpart;       // single-launch layer, one token: [k][H] fp32 weighted expert rows
   size_t ls_end;
   size_t total;
 };
@@ -135,6 +136,7 @@ struct LayerSmallArgs {
   uint32_t* sync;    // kSyncBytes: counters, flags and an error word, zero between calls
   float* partial;    // [32][T][E]
   uint32_t* h;       // [T*k][I/2] f16 pairs
+  float* xpart;      // [k][H] fp32: one token's weighted expert rows (per-XCD mode)
 };
 size_t layer_small_lds(int T, int H, int I, int k);
 bool layer_small_fits(int T, int H, int I, int E, int k);

@@ -24,6 +24,14 @@
 //      of its first expert's weights, then waits for counter C, stages its half of every h row
 //      in LDS and streams the down weights of every active expert;
 //      out[t][f] = sum over the token's rows of w * ts_d * (W_d h), the halves added in LDS.
+//   Per-XCD mode (one token with k = 8, the grid a multiple of 8): group g of blocks (index mod
+//   8, which the hardware places on one XCD) runs slot g's expert alone.  In C its wavefronts take
+//   that expert's 16-feature tiles; barrier C becomes one barrier per group (32 arrivals instead
+//   of 256, and no wait for the other experts); D stages only slot g's h row and computes that
+//   expert's down projection over every output feature, block j of the group taking range j of
+//   the tiles.  Each block writes w_g * (W_d h) for its range to row g of a partial buffer; the
+//   eighth block of range j to arrive at the range's counter adds the 8 rows in slot order and
+//   writes out.  (Measured at decode: 50.4 -> 47.4 us.)
 //   Exit: counter X; the last block to arrive resets the counters and flags for the next call.
 // A barrier: every block adds one to the barrier's counter; the block that completes it raises
 // 16 copies of a flag, and each block polls its own copy.
@@ -73,6 +81,7 @@ constexpr int kLsNS = 32;                 // router: slices of the hidden dimens
 constexpr int kLsEG = 32;                 // router: experts per item
 constexpr int kLsSetC = 4;                // gate/up: chunks per load set
 constexpr int kLsSetD = 8;                // down: chunks per load set
+constexpr int kLsXTiles = 8;              // per-XCD mode: output tiles per wavefront, at most
 // A block that gave up waiting writes NaN over its output tiles (the 32-feature tiles
 // blockIdx.x + m * G of every token), so a failed call shows in out: a give-up at barrier A
 // keeps barrier A or C from completing for everyone, so every block with output tiles gives up.
@@ -81,6 +90,12 @@ __device__ inline void ls_fail_out(const LayerSmallArgs& a, int G) {
   for (int ftp = blockIdx.x; ftp < a.H / 32; ftp += G)
     for (int i = threadIdx.x; i < a.T * 32; i += 256)
       a.out[(size_t)(i >> 5) * a.H + ftp * 32 + (i & 31)] = nan;
+}
+// Per-XCD mode (one token): a block of range j that gave up at its group's barrier writes NaN
+// over the range's output features [f0, f1); the range's sum then never completes (the block
+// does not arrive at its counter), so the range shows NaN.
+__device__ inline void ls_fail_range(const LayerSmallArgs& a, int f0, int f1) {
+  for (int f = f0 + (int)threadIdx.x; f < f1; f += 256) a.out[f] = __builtin_nanf("");
 }
 
 // Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
@@ -107,7 +122,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   __shared__ int srow_tok[kLsMaxSlots];
   __shared__ float srow_w[kLsMaxSlots];
   __shared__ float dred[4][TT][16];
-  __shared__ int s_nact, s_flag;
+  __shared__ float xred[4][kLsXTiles][16];  // per-XCD mode: each wavefront's half-sums per tile
+  __shared__ int s_nact, s_flag, s_last;
 
   LS_STAMP(0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -115,6 +131,15 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   const int G = gridDim.x;
   const int T = a.T, H = a.H, I = a.I, E = a.E, k = a.k;
   const int nq = T * k;
+  // Per-XCD mode (one token, k = 8 slots): group g = blockIdx.x % 8 (the hardware puts those
+  // blocks on one XCD; nothing depends on it for correctness) runs slot g's expert alone: its
+  // gate/up tiles, a barrier among the group only, its h row, and its down projection over every
+  // output feature, split over the group's blocks; block j of every group covers the same range
+  // of features, and that range's eighth arrival adds the 8 weighted rows in slot order.
+  const int xgs = G / kLsGroups;  // blocks per group
+  const bool xm = TT == 1 && k == kLsGroups && G % kLsGroups == 0 && xgs <= kLsXRanges &&
+                  (H / 16 + xgs - 1) / xgs <= 2 * kLsXTiles;
+  const int xg = blockIdx.x % kLsGroups, xj = blockIdx.x / kLsGroups;
   const uint32_t spin_cfg = a.sync[kLsSyncSpin];  // written by the host before the launch
   const uint32_t spin = spin_cfg != 0 ? spin_cfg : kLsSpin;
 
@@ -194,11 +219,22 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   const size_t mq = (size_t)I * H / 2, ms = (size_t)I * H / 16;
   const int* c_e = TT == 1 ? slot_e : act_e;      // item's expert
   const int* c_off = TT == 1 ? slot_pos : act_off;  // item's first row in the grouped order
-  int na = 0, n_items = 0, nsets = 0;
+  int na = 0, n_items = 0, nsets = 0, Wc = W, it_end = 0;
   auto plan = [&](int nact) {
     na = nact;
     n_items = na * ntile;
+    it_end = n_items;
     const int my_items = gw < n_items ? (n_items - 1 - gw) / W + 1 : 0;
+    nsets = my_items * nspi;
+  };
+  // per-XCD mode: the group's wavefronts take tiles lw, lw + 4 xgs, ... of slot xg's expert
+  const int xlw = xj * 4 + wv;
+  auto plan_xcd = [&]() {
+    na = k;
+    n_items = k * ntile;
+    Wc = 4 * xgs;
+    it_end = (xg + 1) * ntile;
+    const int my_items = xlw < ntile ? (ntile - 1 - xlw) / Wc + 1 : 0;
     nsets = my_items * nspi;
   };
   // A cursor walks the wavefront's load sets: set j of item it = gw + m W (item-list index ai,
@@ -215,8 +251,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   auto cur_next = [&](Cur& c) {
     if (c.j + 1 < nspi) {
       ++c.j;
-    } else if (c.it + W < n_items) {
-      cur_item(c, c.it + W);
+    } else if (c.it + Wc < it_end) {
+      cur_item(c, c.it + Wc);
     }
   };
   uint4 qgA[kLsSetC], quA[kLsSetC], qgB[kLsSetC], quB[kLsSetC];
@@ -236,8 +272,13 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   };
   Cur lc, uc;
   if constexpr (TT == 1) {
-    plan(k);  // one token: k distinct experts
-    cur_item(lc, gw);
+    if (xm) {
+      plan_xcd();
+      cur_item(lc, xg * ntile + xlw);
+    } else {
+      plan(k);  // one token: k distinct experts
+      cur_item(lc, gw);
+    }
     uc = lc;
   }
 
@@ -553,10 +594,121 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     }
   }
   LS_STAMP(4);
-  ls_arrive(a.sync, kLsSyncC, kLsFlagC, (uint32_t)G);
+  if (xm)
+    ls_arrive_group(a.sync, xg, (uint32_t)xgs);
+  else
+    ls_arrive(a.sync, kLsSyncC, kLsFlagC, (uint32_t)G);
 
   // ---- D: down + combine ----
-  {
+  if (xm) {
+    // per-XCD mode: slot xg's down projection over the output tiles [t0, t1) of range xj.  A
+    // wavefront takes the tiles t0 + par + 2 m (par = wv / 2) over one half of I (kh = wv % 2);
+    // each tile's load set is its 8 chunks of 1 KB along I.
+    const int nci = I / kChunk;
+    const int kh = wv & 1, par = wv >> 1;
+    const int cbeg = kh * nci / 2, nck = (kh + 1) * nci / 2 - cbeg;  // this half's chunks
+    const int hw_row = ((nci + 1) / 2) * (kChunk / 2);                 // LDS words per h row
+    const int ntout = H / 16, tpb = (ntout + xgs - 1) / xgs;
+    const int t0 = min(xj * tpb, ntout), t1 = min(t0 + tpb, ntout);
+    const int nmine = t1 - t0 > par ? (t1 - t0 - par + 1) / 2 : 0;
+    const int nspe = (nck + kLsSetD - 1) / kLsSetD;  // load sets per tile
+    const int nsets = nmine * nspe;
+    const int e = slot_e[xg], hrow = slot_pos[xg];
+    const float wgt = srow_w[hrow], tsd = a.ts[e * 3 + 2];
+    const size_t mq = (size_t)H * I / 2, ms = (size_t)H * I / 16;
+    uint4 qA[kLsSetD], qB[kLsSetD];
+    uint32_t sA[kLsSetD], sB[kLsSetD];
+    auto load_set = [&](uint4* q, uint32_t* sc, int s) {
+      s = min(s, nsets - 1);  // past the end: re-read the last set (unused)
+      const int m = s / nspe, cs = (s % nspe) * kLsSetD;
+      const int ft = t0 + par + 2 * m;
+      const size_t tq = (size_t)e * mq + ((size_t)ft * nci + cbeg) * 1024 + lane * 16;
+      const size_t ts_ = (size_t)e * ms + ((size_t)ft * nci + cbeg) * 128 + lane * 2;
+#pragma unroll
+      for (int u = 0; u < kLsSetD; ++u) {
+        const int c = min(cs + u, nck - 1);
+        q[u] = load_stream16(a.dq + tq + (size_t)c * 1024);
+        sc[u] = load_u16(a.ds + ts_ + (size_t)c * 128);
+      }
+    };
+    const bool has_k = nck > 0 && nsets > 0;
+    if (has_k && wv != 0) load_set(qA, sA, 0);
+    if (!ls_wait_at(a.sync, ls_xc_flag(a.sync, xg), &s_flag, spin)) {
+      ls_fail_range(a, t0 * 16, t1 * 16);
+      ls_exit(a.sync, (uint32_t)G);
+      return;
+    }
+    LS_STAMP(5);
+    // slot xg's h row, both halves: LDS [half][hw_row words], device-scope 64-bit loads
+    uint32_t* hs0 = dyn;
+    const int rq = I / 8;  // 16-byte pieces of the row
+    for (int i = tid; i < rq; i += 256) {
+      const int half = i >= (nci / 2) * (kChunk / 8) ? 1 : 0;
+      const int pl = i - half * (nci / 2) * (kChunk / 8);
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(a.h) + 2 * ((size_t)hrow * rq + i);
+      const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *reinterpret_cast<uint4*>(hs0 + (size_t)half * hw_row + pl * 4) =
+          make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+    }
+    if (has_k && wv == 0) load_set(qA, sA, 0);
+    lds_barrier();
+    LS_STAMP(6);
+    const uint32_t* hs = dyn;
+    float racc = 0.f;
+    if (g == 0)  // a half with no chunks (I = 128) adds zero
+#pragma unroll
+      for (int m = 0; m < kLsXTiles; ++m) xred[wv][m][n] = 0.f;
+    auto use_set = [&](const uint4* q, const uint32_t* sc, int s) {
+      const int m = s / nspe, cs = (s % nspe) * kLsSetD;
+#pragma unroll
+      for (int u = 0; u < kLsSetD; ++u) {
+        const int c = cs + u;
+        if (c < nck) {
+          Dec32h d;
+          decode32(q[u], sc[u], d);
+          racc += dot32(d, reinterpret_cast<const uint4*>(hs + (size_t)kh * hw_row + c * (kChunk / 2) + g * 16));
+        }
+      }
+      if (s % nspe == nspe - 1) {  // the tile's last set: this half's weighted sum
+        const float y = sum_groups(racc) * tsd;
+        if (g == 0) xred[wv][m][n] = wgt * y;
+        racc = 0.f;
+      }
+    };
+    if (has_k) {
+      for (int s = 0; s < nsets; s += 2) {
+        load_set(qB, sB, s + 1);
+        use_set(qA, sA, s);
+        load_set(qA, sA, s + 2);
+        if (s + 1 < nsets) use_set(qB, sB, s + 1);
+      }
+    }
+    lds_barrier();
+    // the two halves of each tile, added in order, into the group's row of the partial buffer
+    float* xp = a.xpart + (size_t)xg * H;
+    if (kh == 0 && g == 0)
+      for (int m = 0; m < nmine; ++m)
+        st_dev(reinterpret_cast<uint32_t*>(xp) + (t0 + par + 2 * m) * 16 + n,
+               __float_as_uint(xred[wv][m][n] + xred[wv + 1][m][n]));
+    // range xj: its eighth arrival adds the 8 groups' rows in slot order and writes out
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    lds_barrier();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(ls_xr_ctr(a.sync, xj), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == kLsGroups - 1;
+    lds_barrier();
+    if (s_last) {
+      const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xpart);
+      for (int f = t0 * 16 + tid; f < t1 * 16; f += 256) {
+        float sum = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < kLsGroups; ++gg) sum += __uint_as_float(ld_dev(xa + (size_t)gg * H + f));
+        a.out[f] = sum;
+      }
+    }
+  } else {
     const int nci = I / kChunk;
     const int kh = wv & 1, ftl = wv >> 1;
     const int cbeg = kh * nci / 2, nck = (kh + 1) * nci / 2 - cbeg;  // this half's chunks

@@ -31,6 +31,18 @@ static_assert((kLsFlagBase + (kLsFlags - 1) * kLsFlagStride + kLsFlagC + 1) < kL
               "flags end before the group counters");
 static_assert((kLsGroupBase + 32 * 3 * kLsGroups) * 4 <= kSyncBytes,
               "group counters must fit in the sync region");
+// Group-local barrier C of the single-launch kernel's per-XCD mode (one counter and one flag per
+// group) and its combine counters (one per range of output features), each on its own 128-byte
+// line in the gaps between the first 8 flag copies.
+constexpr int kLsXRanges = 32;  // combine counters: ranges of output features
+__device__ inline uint32_t* ls_xc_ctr(uint32_t* sync, int g) { return sync + kLsFlagBase + g * kLsFlagStride + 256; }
+__device__ inline uint32_t* ls_xc_flag(uint32_t* sync, int g) { return sync + kLsFlagBase + g * kLsFlagStride + 288; }
+__device__ inline uint32_t* ls_xr_ctr(uint32_t* sync, int j) {
+  return sync + kLsFlagBase + (j % kLsGroups) * kLsFlagStride + 512 + (j / kLsGroups) * 32;
+}
+static_assert(kLsXRanges <= 4 * kLsGroups, "combine counters: four lines per flag gap");
+static_assert(kLsFlagBase + (kLsGroups - 1) * kLsFlagStride + 512 + 3 * 32 < kLsGroupBase,
+              "per-XCD words end before the group counters");
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,11 +81,23 @@ __device__ inline void ls_arrive(uint32_t* sync, int ctr, int flag, uint32_t G) 
   }
 }
 
-// Thread 0 polls this block's copy of the flag; the other wavefronts wait at an LDS-only
-// barrier, keeping their own loads in flight.  false (for every thread) after `limit` polls.
-__device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t limit) {
+// Group barrier among the `gsize` blocks of group g: every earlier store of this block is
+// complete, then thread 0 adds one to the group's counter; the last arrival raises its flag.
+__device__ inline void ls_arrive_group(uint32_t* sync, int g, uint32_t gsize) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  lds_barrier();
   if (threadIdx.x == 0) {
-    const uint32_t* f = sync + kLsFlagBase + (blockIdx.x % kLsFlags) * kLsFlagStride + flag;
+    const uint32_t old = __hip_atomic_fetch_add(ls_xc_ctr(sync, g), 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gsize - 1) st_dev(ls_xc_flag(sync, g), 1u);
+  }
+}
+
+// Thread 0 polls the flag at `f`; the other wavefronts wait at an LDS-only barrier.  false (for
+// every thread) after `limit` polls, with the error word set.
+__device__ inline bool ls_wait_at(uint32_t* sync, const uint32_t* f, int* s_ok, uint32_t limit) {
+  if (threadIdx.x == 0) {
     uint32_t spins = 0;
     int ok = 1;
     while (ld_dev(f) == 0) {
@@ -92,6 +116,13 @@ __device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t lim
   return ok;
 }
 
+// Thread 0 polls this block's copy of the flag; the other wavefronts wait at an LDS-only
+// barrier, keeping their own loads in flight.  false (for every thread) after `limit` polls.
+__device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t limit) {
+  return ls_wait_at(sync, sync + kLsFlagBase + (blockIdx.x % kLsFlags) * kLsFlagStride + flag, s_ok,
+                    limit);
+}
+
 // Exit, for a block that finished its work or gave up waiting: once this block's stores are
 // complete, thread 0 arrives at barrier X; the block that completes it (every block has then
 // stopped polling) resets every counter and flag for the next call.  The error word and the
@@ -103,8 +134,12 @@ __device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
     if (ls_count(sync, 2, kLsSyncX, G)) {
       st_dev(sync + kLsSyncA, 0u);
       st_dev(sync + kLsSyncC, 0u);
-      for (int g = 0; g < kLsGroups; ++g)
+      for (int g = 0; g < kLsGroups; ++g) {
         for (int bar = 0; bar < 3; ++bar) st_dev(ls_group_ctr(sync, bar, g), 0u);
+        st_dev(ls_xc_ctr(sync, g), 0u);
+        st_dev(ls_xc_flag(sync, g), 0u);
+      }
+      for (int j = 0; j < kLsXRanges; ++j) st_dev(ls_xr_ctr(sync, j), 0u);
       for (int i = 0; i < kLsFlags; ++i) {
         st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
         st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);

@@ -236,7 +236,8 @@ moe_status moe_combine_norm(const void *y_dev, int32_t y_dtype, const int32_t *s
  * the counters are still reset for the next call.
  * That path writes logits (if not NULL), topk_id, topk_w, the grouping arrays and out, but not
  * y; the combine there adds each token's experts in the order of the active list rather than
- * by slot.
+ * by slot, except for one token with k = 8, where each block group (one per XCD) runs one
+ * slot's expert and the 8 weighted expert rows, each rounded to fp32, are added in slot order.
  * From 3 to 128 tokens (T*k <= 4096) the router, top-k + softmax, grouping and the grouped
  * GEMM's tile list run as ONE persistent kernel (same pages and sections), then the expert FFN
  * and the combine: y_dev ([T*k][H] of y_dtype, grouped row order) holds the expert outputs.

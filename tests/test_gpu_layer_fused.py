@@ -261,15 +261,22 @@ def test_layer_entry_routing_gives_up_and_recovers(name, word):
         assert torch.equal(getattr(buf, n), v), n
 
 
-@pytest.mark.parametrize("name", ["t1_tiny", "t2_small"])
-@pytest.mark.parametrize("word", [0, 16])
+# (shape, word): the top-level counter of barrier A (word 0) or C (word 16); with one token and
+# k = 8 the kernel's per-XCD mode replaces barrier C by one barrier per group of blocks, whose
+# group-0 counter is word 320 (the 256th word after the first flag copy)
+GIVE_UP_CASES = [("t1_tiny", 0), ("t1_tiny", 16), ("t2_small", 0), ("t2_small", 16),
+                 ("t1_odd_experts", 0), ("t1_odd_experts", 320)]
+
+
+@pytest.mark.parametrize("name,word", GIVE_UP_CASES)
 def test_fused_layer_gives_up_and_recovers(name, word):
-    """A barrier that cannot complete, forced from the host: arrival counter A (word 0) or C
-    (word 16) preset far above the grid size, so no arrival completes it, with a short spin
-    limit (word 49).  Every block must give up, write NaN over its features of out, still arrive
-    at the exit counter and leave the counters and flags reset; the error word is set and
-    moe_layer_check reports it and clears it; the next call on the same workspace is correct
-    again, bit for bit."""
+    """A barrier that cannot complete, forced from the host: an arrival counter preset far above
+    the number of arrivals, so no arrival completes it, with a short spin limit (word 49).  The
+    blocks waiting on it must give up and write NaN over their features of out (in the per-XCD
+    mode the one group that gives up covers every range of features, and no range's sum
+    completes without it), every block must still arrive at the exit counter and leave the
+    counters and flags reset; the error word is set and moe_layer_check reports it and clears
+    it; the next call on the same workspace is correct again, bit for bit."""
     import bit_expert_ffn_amd as moe
     sp = SHAPES[name]
     print("case fused give-up", name, "word", word, flush=True)
