@@ -12,9 +12,15 @@ namespace moe {
 
 constexpr int kChunk = 128;  // K values per chunk (one tile-major column block)
 
-__device__ inline uint32_t load_u16(const uint8_t* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
+// Lane l's two scale bytes are bytes 2 l and 2 l + 1 of a 128-byte scale block.  They are
+// loaded as the aligned dword that holds them (p = block + 4 (l / 2); lanes 2 i and 2 i + 1 read
+// the same dword) and taken out at the use with scale_pair().  A 16-bit load leaves the compiler
+// a value to zero-extend, and where it placed that at a loop back edge or where two paths join,
+// the wavefront waited there for the whole load set it had just issued.
+__device__ inline uint32_t load_scale_dword(const uint8_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
 }
+__device__ inline uint32_t scale_pair(uint32_t w, int lane) { return w >> ((lane & 1) * 16); }
 
 // 16 bytes of weights that the kernel reads once: a non-temporal load, so that the streamed
 // expert weights do not displace reused lines from the caches (measured: the few-row expert

@@ -64,8 +64,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
   const size_t tile0 = (size_t)rt * nchunk_all + cbeg;
   const uint8_t* gqp = gq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
   const uint8_t* uqp = uq + (size_t)e * ((size_t)I * H / 2) + (tile0 * 64 + lane) * 16;
-  const uint8_t* gsp = gs + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
-  const uint8_t* usp = us + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + lane) * 2;
+  const uint8_t* gsp = gs + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + (lane & ~1)) * 2;
+  const uint8_t* usp = us + (size_t)e * ((size_t)I * H / 16) + (tile0 * 64 + (lane & ~1)) * 2;
   // two sets of kSet chunks alternate: one set's loads are in flight while the other is used
   uint4 qgA[kSet], quA[kSet], qgB[kSet], quB[kSet];
   uint32_t sgA[kSet], suA[kSet], sgB[kSet], suB[kSet];
@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       const int c = min(c0 + u, nchunk - 1);  // clamped: past the end re-reads the last chunk
       qg[u] = load_stream16(gqp + c * 1024);
       qu[u] = load_stream16(uqp + c * 1024);
-      sg[u] = load_u16(gsp + c * 128);
-      su[u] = load_u16(usp + c * 128);
+      sg[u] = load_scale_dword(gsp + c * 128);
+      su[u] = load_scale_dword(usp + c * 128);
     }
   };
   // the first weights depend only on the expert: with few tokens (early != 0) request them
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       const int c = c0 + u;
       if (c < nchunk) {
         Dec32bf dg, du;  // decoded once, dotted with every row
-        decode32(qg[u], sg[u], dg);
-        decode32(qu[u], su[u], du);
+        decode32(qg[u], scale_pair(sg[u], lane), dg);
+        decode32(qu[u], scale_pair(su[u], lane), du);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (r < rows) {
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
   const int nchunk = (ks + 1) * nchunk_all / KS - cbeg;
   const size_t tile0 = (size_t)rt * nchunk_all + cbeg;
   const uint8_t* qp = dq + (size_t)e * ((size_t)H * I / 2) + (tile0 * 64 + lane) * 16;
-  const uint8_t* sp = dsc + (size_t)e * ((size_t)H * I / 16) + (tile0 * 64 + lane) * 2;
+  const uint8_t* sp = dsc + (size_t)e * ((size_t)H * I / 16) + (tile0 * 64 + (lane & ~1)) * 2;
   uint4 qA[kSet], qB[kSet];
   uint32_t sA[kSet], sB[kSet];
   auto load_set = [&](uint4* q, uint32_t* sc, int c0) {
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
     for (int u = 0; u < kSet; ++u) {
       const int c = min(c0 + u, nchunk - 1);
       q[u] = load_stream16(qp + c * 1024);
-      sc[u] = load_u16(sp + c * 128);
+      sc[u] = load_scale_dword(sp + c * 128);
     }
   };
   // first weights before the dependent loads that staging h needs (few tokens only)
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
       const int c = c0 + u;
       if (c < nchunk) {
         Dec32h d;  // decoded once, dotted with every row
-        decode32(q[u], sc[u], d);
+        decode32(q[u], scale_pair(sc[u], lane), d);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           if (r < rows)

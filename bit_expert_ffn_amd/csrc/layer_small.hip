@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   __shared__ int slot_e[kLsMaxSlots], slot_cnt[kLsMaxSlots], slot_first[kLsMaxSlots];
   __shared__ int slot_pos[kLsMaxSlots];
   __shared__ float slot_w[kLsMaxSlots];
+  __shared__ float act_tsd[kLsMaxSlots];  // down tensor scale of each active expert
   __shared__ int act_e[kLsMaxSlots], act_cnt[kLsMaxSlots], act_off[kLsMaxSlots];
   __shared__ int srow_tok[kLsMaxSlots];
   __shared__ float srow_w[kLsMaxSlots];
@@ -260,14 +261,14 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   auto load_set = [&](uint4* qg, uint4* qu, uint32_t* sg, uint32_t* su, const Cur& c, int e) {
     const int cs = c.j * kLsSetC;
     const size_t tq = (size_t)e * mq + ((size_t)c.rt * nch) * 1024 + lane * 16;
-    const size_t ts_ = (size_t)e * ms + ((size_t)c.rt * nch) * 128 + lane * 2;
+    const size_t ts_ = (size_t)e * ms + ((size_t)c.rt * nch) * 128 + (lane >> 1) * 4;
 #pragma unroll
     for (int u = 0; u < kLsSetC; ++u) {
       const int ch = min(cs + u, nch - 1);
       qg[u] = load_stream16(a.gq + tq + (size_t)ch * 1024);
       qu[u] = load_stream16(a.uq + tq + (size_t)ch * 1024);
-      sg[u] = load_u16(a.gs + ts_ + (size_t)ch * 128);
-      su[u] = load_u16(a.us + ts_ + (size_t)ch * 128);
+      sg[u] = load_scale_dword(a.gs + ts_ + (size_t)ch * 128);
+      su[u] = load_scale_dword(a.us + ts_ + (size_t)ch * 128);
     }
   };
   Cur lc, uc;
@@ -538,8 +539,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         const int c = cs + u;
         if (c < nch) {
           Dec32bf dg, du;  // decoded once, dotted with every row
-          decode32(qg[u], sg[u], dg);
-          decode32(qu[u], su[u], du);
+          decode32(qg[u], scale_pair(sg[u], lane), dg);
+          decode32(qu[u], scale_pair(su[u], lane), du);
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
             if (r < rows) {
@@ -594,6 +595,9 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     }
   }
   LS_STAMP(4);
+  // the down phase's tensor scales, read here: a load inside its loop would wait for every
+  // weight load in flight before it
+  if (!xm && tid < na) act_tsd[tid] = a.ts[act_e[tid] * 3 + 2];
   if (xm)
     ls_arrive_group(a.sync, xg, (uint32_t)xgs);
   else
@@ -623,12 +627,12 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       const int m = s / nspe, cs = (s % nspe) * kLsSetD;
       const int ft = t0 + par + 2 * m;
       const size_t tq = (size_t)e * mq + ((size_t)ft * nci + cbeg) * 1024 + lane * 16;
-      const size_t ts_ = (size_t)e * ms + ((size_t)ft * nci + cbeg) * 128 + lane * 2;
+      const size_t ts_ = (size_t)e * ms + ((size_t)ft * nci + cbeg) * 128 + (lane >> 1) * 4;
 #pragma unroll
       for (int u = 0; u < kLsSetD; ++u) {
         const int c = min(cs + u, nck - 1);
         q[u] = load_stream16(a.dq + tq + (size_t)c * 1024);
-        sc[u] = load_u16(a.ds + ts_ + (size_t)c * 128);
+        sc[u] = load_scale_dword(a.ds + ts_ + (size_t)c * 128);
       }
     };
     const bool has_k = nck > 0 && nsets > 0;
@@ -666,7 +670,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         const int c = cs + u;
         if (c < nck) {
           Dec32h d;
-          decode32(q[u], sc[u], d);
+          decode32(q[u], scale_pair(sc[u], lane), d);
           racc += dot32(d, reinterpret_cast<const uint4*>(hs + (size_t)kh * hw_row + c * (kChunk / 2) + g * 16));
         }
       }
@@ -726,12 +730,12 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       const int e = act_e[ai];
       const int ft = ftp * 2 + ftl;
       const size_t tq = (size_t)e * mq + ((size_t)ft * nci + cbeg) * 1024 + lane * 16;
-      const size_t ts_ = (size_t)e * ms + ((size_t)ft * nci + cbeg) * 128 + lane * 2;
+      const size_t ts_ = (size_t)e * ms + ((size_t)ft * nci + cbeg) * 128 + (lane >> 1) * 4;
 #pragma unroll
       for (int u = 0; u < kLsSetD; ++u) {
         const int c = min(cs + u, nck - 1);
         q[u] = load_stream16(a.dq + tq + (size_t)c * 1024);
-        sc[u] = load_u16(a.ds + ts_ + (size_t)c * 128);
+        sc[u] = load_scale_dword(a.ds + ts_ + (size_t)c * 128);
       }
     };
     const bool has_k = nck > 0;
@@ -777,7 +781,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
           const int c = cs + u;
           if (c < nck) {
             Dec32h d;  // decoded once, dotted with every row
-            decode32(q[u], sc[u], d);
+            decode32(q[u], scale_pair(sc[u], lane), d);
 #pragma unroll
             for (int r = 0; r < TT; ++r) {
               if (r < rows) {
@@ -789,7 +793,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
           }
         }
         if (s % nspe == nspe - 1) {  // the expert's last set: weight its rows into the tokens
-          const float tsd = a.ts[act_e[ai] * 3 + 2];
+          const float tsd = act_tsd[ai];
 #pragma unroll
           for (int r = 0; r < TT; ++r) {
             if (r < rows) {
