@@ -33,6 +33,9 @@
 //   eighth block of range j to arrive at the range's counter adds the 8 rows in slot order and
 //   writes out.  (Measured at decode: 50.4 -> 47.4 us.)
 //   Exit: counter X; the last block to arrive resets the counters and flags for the next call.
+//   In the per-XCD mode every block's last act is its arrival at its range's counter, so the
+//   eighth arrival of each range also adds one to a count of finished ranges, and the arrival
+//   that completes that count resets everything: no exit barrier behind the sums.
 // A barrier: every block adds one to the barrier's counter; the block that completes it raises
 // 16 copies of a flag, and each block polls its own copy.
 // Failure: every wait is bounded (word kLsSyncSpin of the sync region, if non-zero, sets the
@@ -40,7 +43,10 @@
 // writes NaN over its output tiles, skips the rest of its work and still arrives at counter X,
 // so the last block to exit resets the counters and flags whether or not the call succeeded: a
 // failed call leaves NaN in out and the error word set, but cannot leave a barrier
-// half-counted for the next call.
+// half-counted for the next call.  In the per-XCD mode a block that gives up writes NaN over
+// its features of h (at barrier A) and over its row of the partial buffer, and still makes
+// every arrival it has left (group barrier C, its range), so every range's sum is NaN where a
+// block gave up and the count of finished ranges still completes.
 // Data that crosses blocks (partial logits, h) is written with device-scope stores, which write
 // through the per-XCD L2s (not coherent with each other) to memory, and read after the barrier
 // with device-scope loads (global_load sc1), which do not take a possibly stale line from the
@@ -90,12 +96,6 @@ __device__ inline void ls_fail_out(const LayerSmallArgs& a, int G) {
   for (int ftp = blockIdx.x; ftp < a.H / 32; ftp += G)
     for (int i = threadIdx.x; i < a.T * 32; i += 256)
       a.out[(size_t)(i >> 5) * a.H + ftp * 32 + (i & 31)] = nan;
-}
-// Per-XCD mode (one token): a block of range j that gave up at its group's barrier writes NaN
-// over the range's output features [f0, f1); the range's sum then never completes (the block
-// does not arrive at its counter), so the range shows NaN.
-__device__ inline void ls_fail_range(const LayerSmallArgs& a, int f0, int f1) {
-  for (int f = f0 + (int)threadIdx.x; f < f1; f += 256) a.out[f] = __builtin_nanf("");
 }
 
 // Wavefront sum of the device library (ockl): the sum over all active lanes, in every lane.
@@ -283,8 +283,57 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     uc = lc;
   }
 
+  // Per-XCD mode: range xj of the output tiles, [xt0, xt1).
+  const int xtpb = (H / 16 + xgs - 1) / xgs;
+  const int xt0 = min(xj * xtpb, H / 16), xt1 = min(xt0 + xtpb, H / 16);
+  // Per-XCD mode, the end of every block, also of one that gave up: once its row of the partial
+  // buffer is complete, it arrives at range xj's counter; the range's eighth arrival adds the 8
+  // rows in slot order, writes out and counts the range as done, and the arrival that completes
+  // the last range resets the counters and flags.  A block arrives there after its last wait and
+  // after its flag stores are complete, so no exit barrier is needed.
+  auto xm_finish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    lds_barrier();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(ls_xr_ctr(a.sync, xj), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == kLsGroups - 1;
+    lds_barrier();
+    if (s_last) {
+      uint32_t done = 0;
+      if (tid == 0)
+        done = __hip_atomic_fetch_add(ls_xdone(a.sync), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xpart);
+      for (int f = xt0 * 16 + tid; f < xt1 * 16; f += 256) {
+        float sum = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < kLsGroups; ++gg) sum += __uint_as_float(ld_dev(xa + (size_t)gg * H + f));
+        a.out[f] = sum;
+      }
+      if (tid == 0 && done == (uint32_t)xgs - 1) ls_reset(a.sync);
+    }
+  };
+  // Per-XCD mode, a block that gave up: NaN over its row of the partial buffer in range xj, so
+  // that the range's sum is NaN.
+  auto xm_fail_part = [&]() {
+    for (int f = xt0 * 16 + tid; f < xt1 * 16; f += 256)
+      st_dev(reinterpret_cast<uint32_t*>(a.xpart) + (size_t)xg * H + f, 0x7fc00000u);
+  };
+
   // ---- B: logits, top-k, softmax, grouping (every block) ----
   if (!ls_wait(a.sync, kLsFlagA, &s_flag, spin)) {
+    if (xm) {
+      // NaN over this block's gate/up features in every row of h (the rows' order is not known),
+      // so that every block of the group computes NaN; then its arrivals at barrier C and at its
+      // range, as if it had finished
+      for (int rt = xlw; rt < ntile; rt += Wc)
+        for (int r = g; r < k; r += 4)
+          if ((n & 1) == 0) st_dev(a.h + ((size_t)r * I + rt * 16 + n) / 2, 0x7e007e00u);
+      ls_arrive_group(a.sync, xg, (uint32_t)xgs);
+      xm_fail_part();
+      xm_finish();
+      return;
+    }
     ls_fail_out(a, G);
     ls_exit(a.sync, (uint32_t)G);
     return;
@@ -612,8 +661,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     const int kh = wv & 1, par = wv >> 1;
     const int cbeg = kh * nci / 2, nck = (kh + 1) * nci / 2 - cbeg;  // this half's chunks
     const int hw_row = ((nci + 1) / 2) * (kChunk / 2);                 // LDS words per h row
-    const int ntout = H / 16, tpb = (ntout + xgs - 1) / xgs;
-    const int t0 = min(xj * tpb, ntout), t1 = min(t0 + tpb, ntout);
+    const int t0 = xt0, t1 = xt1;
     const int nmine = t1 - t0 > par ? (t1 - t0 - par + 1) / 2 : 0;
     const int nspe = (nck + kLsSetD - 1) / kLsSetD;  // load sets per tile
     const int nsets = nmine * nspe;
@@ -638,8 +686,8 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
     const bool has_k = nck > 0 && nsets > 0;
     if (has_k && wv != 0) load_set(qA, sA, 0);
     if (!ls_wait_at(a.sync, ls_xc_flag(a.sync, xg), &s_flag, spin)) {
-      ls_fail_range(a, t0 * 16, t1 * 16);
-      ls_exit(a.sync, (uint32_t)G);
+      xm_fail_part();
+      xm_finish();
       return;
     }
     LS_STAMP(5);
@@ -695,23 +743,9 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       for (int m = 0; m < nmine; ++m)
         st_dev(reinterpret_cast<uint32_t*>(xp) + (t0 + par + 2 * m) * 16 + n,
                __float_as_uint(xred[wv][m][n] + xred[wv + 1][m][n]));
-    // range xj: its eighth arrival adds the 8 groups' rows in slot order and writes out
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    lds_barrier();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(ls_xr_ctr(a.sync, xj), 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == kLsGroups - 1;
-    lds_barrier();
-    if (s_last) {
-      const uint32_t* xa = reinterpret_cast<const uint32_t*>(a.xpart);
-      for (int f = t0 * 16 + tid; f < t1 * 16; f += 256) {
-        float sum = 0.f;
-#pragma unroll
-        for (int gg = 0; gg < kLsGroups; ++gg) sum += __uint_as_float(ld_dev(xa + (size_t)gg * H + f));
-        a.out[f] = sum;
-      }
-    }
+    LS_STAMP(7);
+    xm_finish();
+    return;
   } else {
     const int nci = I / kChunk;
     const int kh = wv & 1, ftl = wv >> 1;

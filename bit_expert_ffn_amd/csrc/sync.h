@@ -14,7 +14,9 @@
 // is a relaxed device-scope one, issued after a full s_waitcnt so that the block's earlier
 // device-scope stores are complete.  Every wait is bounded.  At the exit every block arrives
 // at barrier X the same way, and the block that completes it resets every counter and flag:
-// every call leaves them zero, whether or not its waits gave up.
+// every call leaves them zero, whether or not its waits gave up.  (The single-launch kernel's
+// per-XCD mode ends on its range counters instead: the arrival that completes the last range
+// resets.)
 #pragma once
 #include "common.h"
 
@@ -40,6 +42,8 @@ __device__ inline uint32_t* ls_xc_flag(uint32_t* sync, int g) { return sync + kL
 __device__ inline uint32_t* ls_xr_ctr(uint32_t* sync, int j) {
   return sync + kLsFlagBase + (j % kLsGroups) * kLsFlagStride + 512 + (j / kLsGroups) * 32;
 }
+// Per-XCD mode: ranges whose sum is complete (the arrival that completes the last one resets).
+__device__ inline uint32_t* ls_xdone(uint32_t* sync) { return sync + kLsFlagBase + 640; }
 static_assert(kLsXRanges <= 4 * kLsGroups, "combine counters: four lines per flag gap");
 static_assert(kLsFlagBase + (kLsGroups - 1) * kLsFlagStride + 512 + 3 * 32 < kLsGroupBase,
               "per-XCD words end before the group counters");
@@ -123,29 +127,34 @@ __device__ inline bool ls_wait(uint32_t* sync, int flag, int* s_ok, uint32_t lim
                     limit);
 }
 
+// Resets every counter and flag for the next call; called by one thread, once every block has
+// stopped polling and every flag store is complete.  The error word and the spin-limit word are
+// left as they are.
+__device__ inline void ls_reset(uint32_t* sync) {
+  st_dev(sync + kLsSyncA, 0u);
+  st_dev(sync + kLsSyncC, 0u);
+  for (int g = 0; g < kLsGroups; ++g) {
+    for (int bar = 0; bar < 3; ++bar) st_dev(ls_group_ctr(sync, bar, g), 0u);
+    st_dev(ls_xc_ctr(sync, g), 0u);
+    st_dev(ls_xc_flag(sync, g), 0u);
+  }
+  for (int j = 0; j < kLsXRanges; ++j) st_dev(ls_xr_ctr(sync, j), 0u);
+  st_dev(ls_xdone(sync), 0u);
+  for (int i = 0; i < kLsFlags; ++i) {
+    st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
+    st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
+  }
+  st_dev(sync + kLsSyncX, 0u);
+}
+
 // Exit, for a block that finished its work or gave up waiting: once this block's stores are
 // complete, thread 0 arrives at barrier X; the block that completes it (every block has then
-// stopped polling) resets every counter and flag for the next call.  The error word and the
-// spin-limit word are left as they are.
+// stopped polling) resets every counter and flag for the next call.
 __device__ inline void ls_exit(uint32_t* sync, uint32_t G) {
   if (threadIdx.x == 0) {
     __builtin_amdgcn_s_waitcnt(0);  // this block's flag stores are complete
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (ls_count(sync, 2, kLsSyncX, G)) {
-      st_dev(sync + kLsSyncA, 0u);
-      st_dev(sync + kLsSyncC, 0u);
-      for (int g = 0; g < kLsGroups; ++g) {
-        for (int bar = 0; bar < 3; ++bar) st_dev(ls_group_ctr(sync, bar, g), 0u);
-        st_dev(ls_xc_ctr(sync, g), 0u);
-        st_dev(ls_xc_flag(sync, g), 0u);
-      }
-      for (int j = 0; j < kLsXRanges; ++j) st_dev(ls_xr_ctr(sync, j), 0u);
-      for (int i = 0; i < kLsFlags; ++i) {
-        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagA, 0u);
-        st_dev(sync + kLsFlagBase + i * kLsFlagStride + kLsFlagC, 0u);
-      }
-      st_dev(sync + kLsSyncX, 0u);
-    }
+    if (ls_count(sync, 2, kLsSyncX, G)) ls_reset(sync);
   }
 }
 

@@ -273,10 +273,11 @@ def test_fused_layer_gives_up_and_recovers(name, word):
     """A barrier that cannot complete, forced from the host: an arrival counter preset far above
     the number of arrivals, so no arrival completes it, with a short spin limit (word 49).  The
     blocks waiting on it must give up and write NaN over their features of out (in the per-XCD
-    mode the one group that gives up covers every range of features, and no range's sum
-    completes without it), every block must still arrive at the exit counter and leave the
-    counters and flags reset; the error word is set and moe_layer_check reports it and clears
-    it; the next call on the same workspace is correct again, bit for bit."""
+    mode they write NaN into their rows of the partial buffer, and the one group that gives up
+    covers every range of features), every block must still make its remaining arrivals (the
+    exit counter, or in the per-XCD mode its range counter) and leave the counters and flags
+    reset; the error word is set and moe_layer_check reports it and clears it; the next call on
+    the same workspace is correct again, bit for bit."""
     import bit_expert_ffn_amd as moe
     sp = SHAPES[name]
     print("case fused give-up", name, "word", word, flush=True)
