@@ -69,7 +69,8 @@ namespace moe {
 // moe_timeline_layer_small.  Slots: 0 entry, 1 router partials stored, 2 barrier A passed,
 // 3 routing published (gate/up starts), 4 gate/up done, 5 barrier C passed, 6 h staged, 7 exit;
 // inside the routing: 8 logits summed, 9 first-level ranks, 10 candidate ranks, 11 first gate/up
-// sets issued (one token).
+// sets issued (one token); in the per-XCD down phase: 12 first set used, 13 last set used,
+// 14 range counter passed.
 #ifdef MOE_TIMELINE
 __device__ unsigned long long g_ls_timeline[1024][16];
 #define LS_STAMP(i)                                                                 \
@@ -299,6 +300,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       s_last = __hip_atomic_fetch_add(ls_xr_ctr(a.sync, xj), 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT) == kLsGroups - 1;
     lds_barrier();
+    LS_STAMP(14);
     if (s_last) {
       uint32_t done = 0;
       if (tid == 0)
@@ -732,10 +734,12 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       for (int s = 0; s < nsets; s += 2) {
         load_set(qB, sB, s + 1);
         use_set(qA, sA, s);
+        if (s == 0) LS_STAMP(12);
         load_set(qA, sA, s + 2);
         if (s + 1 < nsets) use_set(qB, sB, s + 1);
       }
     }
+    LS_STAMP(13);
     lds_barrier();
     // the two halves of each tile, added in order, into the group's row of the partial buffer
     float* xp = a.xpart + (size_t)xg * H;

@@ -49,9 +49,9 @@ namespace moe {
 // 100 MHz real-time counter at the phase boundaries of the last call, read back with
 // moe_timeline_route_group.  Slots: 0 entry, 1 router partials stored, 2 barrier A passed (token
 // blocks), 3 top-k done, 4 barrier C passed, 5 rows placed, 6 block 0: active list sorted,
-// 7 exit.
+// 7 exit; inside phase A: 8 first loads issued, 9 products done, 10 sums in LDS.
 #ifdef MOE_TIMELINE
-__device__ unsigned long long g_rg_timeline[1024][8];
+__device__ unsigned long long g_rg_timeline[1024][16];
 #define RG_STAMP(i)                                                                 \
   do {                                                                              \
     if (threadIdx.x == 0 && blockIdx.x < 1024)                                      \
@@ -160,7 +160,10 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
     const int nst = H / 16;  // 16-position steps of the hidden dimension
     const int r32 = lane & 31, kg = lane >> 5;
     for (int it = blockIdx.x; it < kRgSlices * NEG; it += G) {
-      const int sl = it / NEG, eg = it - sl * NEG;
+      // item it -> (slice, expert group): the NEG items of one slice get the same it % 8, so
+      // they run on one XCD and share the slice's x rows in its L2
+      const int j8 = it >> 3;
+      const int sl = (it & 7) + 8 * (j8 / NEG), eg = j8 % NEG;
       const int s0 = sl * nst / kRgSlices, s1 = (sl + 1) * nst / kRgSlices;
       const int e = min(eg * kRgEG + r32, E - 1);  // clamped columns are not stored
       f32x16 acc[TTT];
@@ -186,6 +189,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
             xa[b][i] = *reinterpret_cast<const rg_u32x4*>(a.x + (size_t)t * H + h0);
           }
         }
+        if (sb == s0 + wv) RG_STAMP(8);
 #pragma unroll
         for (int b = 0; b < kRgBatch; ++b) {
           if (sb + 4 * b < s1) {
@@ -210,6 +214,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
           }
         }
       }
+      RG_STAMP(9);
       // accumulator element v of lane l: token (v / 4) * 8 + (l / 32) * 4 + v % 4 of its tile,
       // expert l % 32 of the item
 #pragma unroll
@@ -217,6 +222,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) red[wv][i * 32 + (v >> 2) * 8 + kg * 4 + (v & 3)][r32] = acc[i][v];
       __syncthreads();
+      RG_STAMP(10);
       for (int q = tid; q < TTT * 32 * kRgEG; q += 256) {
         const int t = q / kRgEG, el = q - t * kRgEG, ee = eg * kRgEG + el;
         const float s = ((red[0][t][el] + red[1][t][el]) + red[2][t][el]) + red[3][t][el];

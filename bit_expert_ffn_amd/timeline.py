@@ -26,12 +26,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 LAYER_SMALL = ["entry", "router partials stored", "barrier A passed", "routing published, gate/up starts",
                "gate/up done", "barrier C passed", "h staged", "exit", "logits summed", "first-level ranks",
-               "candidate ranks (top-k known)", "first gate/up sets issued"]
-LAYER_SMALL_ORDER = [0, 1, 2, 8, 9, 10, 11, 3, 4, 5, 6, 7]
+               "candidate ranks (top-k known)", "first gate/up sets issued", "first down set used",
+               "last down set used", "range counter passed"]
+LAYER_SMALL_ORDER = [0, 1, 2, 8, 9, 10, 11, 3, 4, 5, 6, 12, 13, 7, 14]
 ROUTE_GROUP = ["entry", "router partials stored", "barrier A passed", "top-k done", "barrier C passed",
-               "rows placed", "active list sorted", "exit"]
+               "rows placed", "active list sorted", "exit", "router loads issued", "router products done",
+               "router sums in LDS"]
+ROUTE_GROUP_ORDER = [0, 8, 9, 10, 1, 2, 3, 4, 5, 6, 7]
 # blocks that record each slot of the fused routing kernel: all, or the T token blocks, or block 0
-ROUTE_GROUP_BLOCKS = ["all", "all", "token", "token", "token", "token", "block 0", "all"]
+ROUTE_GROUP_BLOCKS = ["all", "all", "token", "token", "token", "token", "block 0", "all", "all", "all", "all"]
 
 
 def main():
@@ -83,7 +86,7 @@ def main():
             calls[i % pool]()
             i += 1
         torch.cuda.synchronize()
-        h = np.zeros((1024, 16 if small else 8), np.uint64)
+        h = np.zeros((1024, 16), np.uint64)
         if read(ctypes.c_void_p(h.ctypes.data)) != 0:
             sys.exit("reading the timeline failed")
         runs.append(h)
@@ -99,7 +102,7 @@ def main():
     rel = np.stack(rel)  # [calls][blocks][slots]
     print("%s: %s, T=%d, %d blocks, %d calls (us from the first block's entry)" % (
         "layer_small_kernel" if small else "route_group_kernel", args.workload, T, G, args.calls))
-    for j in (LAYER_SMALL_ORDER if small else range(len(names))):
+    for j in (LAYER_SMALL_ORDER if small else ROUTE_GROUP_ORDER):
         name = names[j]
         who = "all" if small else ROUTE_GROUP_BLOCKS[j]
         v = rel[:, :T, j] if who == "token" else rel[:, :1, j] if who == "block 0" else rel[:, :, j]
