@@ -33,6 +33,8 @@
 //   eighth block of range j to arrive at the range's counter adds the 8 rows in slot order and
 //   writes out.  (Measured at decode: 50.4 -> 47.4 us.)
 //   Exit: counter X; the last block to arrive resets the counters and flags for the next call.
+//   A block arrives there once it has passed its last wait (barrier C, for a block with output
+//   tiles), before its down phase, so that the reset overlaps the down phase.
 //   In the per-XCD mode every block's last act is its arrival at its range's counter, so the
 //   eighth arrival of each range also adds one to a count of finished ranges, and the arrival
 //   that completes that count resets everything: no exit barrier behind the sums.
@@ -777,6 +779,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       }
     };
     const bool has_k = nck > 0;
+    bool exited = false;
     // a block with no output tile neither waits nor stages h
     if (ftp < npairs) {
       // the first weights are requested before waiting for h (not by the polling wavefront,
@@ -788,6 +791,10 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         return;
       }
       LS_STAMP(5);
+      // the block's last wait is over and its flag stores are complete: it arrives at the exit
+      // barrier now, so that the reset overlaps the down phase instead of following it
+      ls_exit(a.sync, (uint32_t)G);
+      exited = true;
       if (has_k && wv == 0) load_set(qA, sA, 0);
       // both halves of every h row: LDS [half][row][hw_row words], read with device-scope
       // 64-bit loads (the rows were written by other blocks)
@@ -868,11 +875,10 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       }
       lds_barrier();
     }
+    // ---- exit: a block that has not arrived at the exit barrier yet (no output tile) ----
+    LS_STAMP(7);
+    if (!exited) ls_exit(a.sync, (uint32_t)G);
   }
-
-  // ---- exit: the last block resets the counters and flags for the next call ----
-  LS_STAMP(7);
-  ls_exit(a.sync, (uint32_t)G);
 }
 
 size_t layer_small_lds(int T, int H, int I, int k) {

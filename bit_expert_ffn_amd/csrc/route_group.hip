@@ -31,6 +31,9 @@
 //      its own k rows; block 0 also writes the counts and offsets, the active experts sorted by
 //      (count desc, id asc) (a bitonic sort of count << 8 | (255 - id)) and the grouped GEMM's
 //      row tiles.
+//   Exit barrier X (its last arrival resets the counters and flags): a token block arrives as
+//   soon as it has passed barrier C, its last wait, and before its stores of phase C, so that
+//   the reset overlaps them; the other blocks arrive after barrier C's arrival.
 // A wait that gives up sets the error word (as in the single-launch layer); block 0 then writes
 // a grouping with no active expert, identity slot rows and NaN weights, so the kernels that
 // follow stay inside their buffers and out shows NaN.
@@ -297,6 +300,9 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
       ls_exit(a.sync, (uint32_t)G);
       return;
     }
+    // this block's last wait is over and its flag stores are complete: it arrives at the exit
+    // barrier now, so that the reset overlaps the stores below instead of following them
+    ls_exit(a.sync, (uint32_t)G);
     RG_STAMP(4);
     const int mw = (T + 31) >> 5;  // mask words in use
     int c = 0;
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void route_group_kernel(RouteGroupArgs a) {
     }
   }
   RG_STAMP(7);
-  ls_exit(a.sync, (uint32_t)G);
+  if (t >= T) ls_exit(a.sync, (uint32_t)G);
 }
 
 bool route_group_fits(int T, int k) {
