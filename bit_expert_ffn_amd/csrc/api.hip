@@ -19,7 +19,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int k) {
   L.route_partial = base;
   L.route_wsplit = base + align_up((size_t)p.KS * T * E * sizeof(float), 256);
   L.route_end = L.route_wsplit;
-  if (p.mfma) L.route_end += align_up((size_t)3 * E * H * sizeof(uint16_t), 256);
+  if (p.mfma) L.route_end += align_up((size_t)3 * ((E + 31) / 32 * 32) * H * sizeof(uint16_t), 256);
   const size_t n = (size_t)T * k;
   L.group_whist = base;
   L.group_end = 0;

@@ -42,7 +42,7 @@ constexpr int kSyncErrWord = 48;
 constexpr int kSyncSpinWord = 49;
 struct WsLayout {
   size_t route_partial;  // [KS][T][E] fp32
-  size_t route_wsplit;   // [3][E][H] bf16 (matrix-core router only)
+  size_t route_wsplit;   // 3 x ceil(E / 32) x 32 x H bf16, operand order (matrix-core router only)
   size_t route_end;
   size_t group_whist;    // [nblk*16][E] int32 (three-pass grouping only)
   size_t group_end;

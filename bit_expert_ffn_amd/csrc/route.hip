@@ -20,10 +20,10 @@
 //
 // Many tokens (T >= kRouteMfmaMinT): the slices come from the matrix cores instead.
 //   router_split_kernel   writes each fp32 router weight as the exact sum of three bf16 values
-//       (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid), transposed to [3][E][H] so that
-//       8 consecutive hidden positions of one expert are 16 contiguous bytes.
+//       (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid), in the order the matrix-core
+//       operand reads them (1 KB per 32 experts x 16 hidden positions).
 //   router_mfma_kernel    block = 128 tokens x 256 experts (4 wavefronts of 64 experts) over one
-//       slice of the hidden dimension; logits += x * hi + x * mid + x * lo on
+//       slice of the hidden dimension, x staged in LDS; logits += x * hi + x * mid + x * lo on
 //       v_mfma_f32_32x32x16_bf16.  x is bf16, so every product is exact in fp32 and the result
 //       differs from the fp32 definition only in the order of the fp32 additions.
 #include "common.h"
@@ -156,12 +156,17 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// wr [H][E] fp32 -> wsplit [3][E][H] bf16 with w = hi + mid + lo exactly: hi keeps the leading
+// wr [H][E] fp32 -> wsplit: three bf16 planes with w = hi + mid + lo exactly: hi keeps the leading
 // 8 significant bits (rounded), the residual w - hi is exact in fp32 and has at most 16
 // significant bits, mid keeps 8 of them and the remaining w - hi - mid fits in lo.
+// Each plane is stored in the order the matrix-core operand reads it: for the 32-expert tile et
+// and the 16-position step st, 1 KB holds lane l's 8 values at byte 16 l (expert 32 et + l % 32,
+// positions 16 st + 8 (l / 32) .. + 7), so one wavefront's operand of one step is one coalesced
+// 1 KB load.  Element offset (((p NET + et) NST + st) 64 + l) 8 + j, NET = ceil(E / 32), NST =
+// H / 16; the experts past E in the last tile are zero.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int H,
                                                            int E, uint16_t* __restrict__ wsplit) {
-  __shared__ float tile[64][65];
+  __shared__ float tile[64][65];  // [position][expert]
   const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int hh = i >> 6, ee = i & 63;
@@ -170,68 +175,97 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     tile[hh][ee] = v;
   }
   __syncthreads();
-  const size_t plane = (size_t)E * H;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ee = i >> 6, hh = i & 63;
-    if (h0 + hh < H && e0 + ee < E) {
-      const float v = tile[hh][ee];
-      const uint16_t hi = f32_to_bf16_rne(v);
-      const float r1 = v - bf16_to_f32(hi);
-      const uint16_t mid = f32_to_bf16_rne(r1);
-      const float r2 = r1 - bf16_to_f32(mid);
-      const uint16_t lo = f32_to_bf16_rne(r2);
-      const size_t o = (size_t)(e0 + ee) * H + h0 + hh;
-      wsplit[o] = hi;
-      wsplit[plane + o] = mid;
-      wsplit[2 * plane + o] = lo;
+  const int NET = (E + 31) / 32, NST = H / 16;
+  const size_t plane = (size_t)NET * 32 * H;
+  // item = (expert ee of the tile, 8-position group hg): two per thread
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int ee = i & 63, hg = i >> 6;
+    const int e = e0 + ee, h = h0 + hg * 8;
+    if (e >= NET * 32 || h >= H) continue;
+    uint32_t pk[3][4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t q[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const float v = tile[hg * 8 + j + jj][ee];
+        const uint16_t hi = f32_to_bf16_rne(v);
+        const float r1 = v - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        const uint16_t lo = f32_to_bf16_rne(r2);
+        q[0] |= (uint32_t)hi << (16 * jj);
+        q[1] |= (uint32_t)mid << (16 * jj);
+        q[2] |= (uint32_t)lo << (16 * jj);
+      }
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) pk[pp][j / 2] = q[pp];
     }
+    const int et = e >> 5, st = h >> 4, l = ((h >> 3) & 1) * 32 + (e & 31);
+    const size_t o = (((size_t)et * NST + st) * 64 + l) * 8;
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+      *reinterpret_cast<uint4*>(wsplit + pp * plane + o) = make_uint4(pk[pp][0], pk[pp][1], pk[pp][2], pk[pp][3]);
   }
 }
 
 // Block: 4 wavefronts, 128 tokens; wavefront w takes experts 64 w .. 64 w + 63 (two 32-expert
 // tiles) for all 128 tokens (four 32-token tiles), over hidden positions [ks kc, ks kc + kc).
-// MFMA operands straight from memory: lane l holds token (or expert) l % 32 and 8 consecutive
-// hidden positions 8 (l / 32) .. of the 16-position step.  Rows past T or E are clamped (their
-// results are not stored).  No LDS and no barriers: a wavefront with no experts returns.
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+// x goes through LDS: the block loads each 64-position chunk of its 128 token rows once, with
+// coalesced 16-byte loads, double-buffered (the next chunk's loads are in flight during the
+// current chunk's products), and every wavefront reads its A operands (lane l: token l % 32, 8
+// positions from 8 (l / 32)) from there.  The split weights are read in operand order, one
+// coalesced 1 KB load per operand, one step ahead.  Token rows past T are clamped and experts
+// past E are zero; neither is stored.  A wavefront with no experts still loads x and meets the
+// barriers.
+constexpr int kRmChunk = 64;         // positions per x chunk in LDS
+constexpr int kRmXS = kRmChunk + 8;  // bf16 per LDS row (padded: conflict-free 16-byte reads)
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wsplit,
                                                           int T, int H, int E, int kc,
                                                           float* __restrict__ partial) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][128 * kRmXS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int e_base = w * 64;
-  if (e_base >= E) return;
+  const bool has_e = e_base < E;
   const int t0 = blockIdx.x * 128, ks = blockIdx.y;
   const int k_begin = ks * kc, k_end = min(H, k_begin + kc);
-  const int nsteps = (k_end - k_begin) / 16;  // even: kc and H are multiples of 128
+  const int nsteps = (k_end - k_begin) / 16;  // a multiple of 8: kc and H are multiples of 128
+  const int nchunks = nsteps / 4;
   const int r32 = lane & 31, kg = lane >> 5;
-  const uint16_t* xr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    xr[i] = x + (size_t)min(t0 + i * 32 + r32, T - 1) * H + k_begin + kg * 8;
-  const size_t plane = (size_t)E * H;
-  uint32_t woff[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-    woff[n] = (uint32_t)min(e_base + n * 32 + r32, E - 1) * (uint32_t)H + k_begin + kg * 8;
-  const uint16_t* w0 = wsplit;
-  const uint16_t* w1 = wsplit + plane;
-  const uint16_t* w2 = wsplit + 2 * plane;
+  const int NET = (E + 31) / 32, NST = H / 16;
+  const size_t plane = (size_t)NET * 32 * H;
+  const int et0 = min(2 * w, NET - 1), et1 = min(2 * w + 1, NET - 1);
+  const uint16_t* wb0 = wsplit + ((size_t)et0 * NST + k_begin / 16) * 512 + lane * 8;
+  const uint16_t* wb1 = wsplit + ((size_t)et1 * NST + k_begin / 16) * 512 + lane * 8;
 
+  // x chunk c: piece q = tid + 256 u is row q / 8, 16-byte piece q % 8 of the chunk
+  u32x4 xv[4];
+  auto load_x = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u, row = q >> 3, pc = q & 7;
+      xv[u] = *reinterpret_cast<const u32x4*>(x + (size_t)min(t0 + row, T - 1) * H + k_begin +
+                                             c * kRmChunk + pc * 8);
+    }
+  };
+  auto store_x = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + 256 * u, row = q >> 3, pc = q & 7;
+      *reinterpret_cast<u32x4*>(&xs[buf][row * kRmXS + pc * 8]) = xv[u];
+    }
+  };
   struct Regs {
-    u32x4 a[4];
     u32x4 b[3][2];
   };
-  auto load = [&](Regs& r, int step) __attribute__((always_inline)) {
-    const uint32_t k = (uint32_t)step * 16;
+  auto load_b = [&](Regs& r, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(xr[i] + k);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      r.b[0][n] = *reinterpret_cast<const u32x4*>(w0 + (woff[n] + k));
-      r.b[1][n] = *reinterpret_cast<const u32x4*>(w1 + (woff[n] + k));
-      r.b[2][n] = *reinterpret_cast<const u32x4*>(w2 + (woff[n] + k));
+    for (int pp = 0; pp < 3; ++pp) {
+      r.b[pp][0] = *reinterpret_cast<const u32x4*>(wb0 + pp * plane + (size_t)st * 512);
+      r.b[pp][1] = *reinterpret_cast<const u32x4*>(wb1 + pp * plane + (size_t)st * 512);
     }
   };
   f32x16 acc[4][2];
@@ -241,31 +275,47 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][n][v] = 0.f;
-  auto compute = [&](const Regs& r) __attribute__((always_inline)) {
+  auto compute = [&](const Regs& r, int buf, int sc) __attribute__((always_inline)) {
+    u32x4 a[4];
 #pragma unroll
-    for (int p = 2; p >= 0; --p)  // small pieces first
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const u32x4*>(&xs[buf][(i * 32 + r32) * kRmXS + sc * 16 + kg * 8]);
+#pragma unroll
+    for (int pp = 2; pp >= 0; --pp)  // small pieces first
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int n = 0; n < 2; ++n)
           acc[i][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, r.a[i]), __builtin_bit_cast(bf16x8, r.b[p][n]),
-              acc[i][n], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, r.b[pp][n]), acc[i][n], 0, 0, 0);
   };
-  // one step of loads in flight behind the MFMAs; the scheduling barriers keep the compiler
-  // from sinking the loads next to their first use
   Regs r0, r1;
-  load(r0, 0);
-  for (int st = 0; st < nsteps; st += 2) {
-    load(r1, st + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(r0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(r0, min(st + 2, nsteps - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(r1);
-    __builtin_amdgcn_sched_barrier(0);
+  load_x(0);
+  if (has_e) load_b(r0, 0);
+  store_x(0);
+  if (nchunks > 1) load_x(1);
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();  // chunk c is in xs[c & 1]; the other buffer's chunk has been used
+    if (c + 1 < nchunks) {
+      store_x((c + 1) & 1);
+      if (c + 2 < nchunks) load_x(c + 2);
+    }
+    if (has_e) {
+#pragma unroll
+      for (int sc = 0; sc < 4; sc += 2) {
+        const int st = c * 4 + sc;
+        load_b(r1, st + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(r0, c & 1, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(r0, min(st + 2, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(r1, c & 1, sc + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
+  if (!has_e) return;
   // accumulator element v of a 32x32 tile: token (v/4)*8 + (lane/32)*4 + v%4, expert lane % 32
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -368,7 +418,7 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   const RoutePlan p = route_plan(T, H, E);
   dim3 grid(p.tiles, p.KS);
   if (p.mfma) {
-    router_split_kernel<<<dim3(H / 64, (E + 63) / 64), 256, 0, s>>>(wr, H, E, wsplit);
+    router_split_kernel<<<dim3(H / 64, ((E + 31) / 32 * 32 + 63) / 64), 256, 0, s>>>(wr, H, E, wsplit);
     router_mfma_kernel<<<grid, 256, 0, s>>>(x, wsplit, T, H, E, p.kc, partial);
   } else {
 #define MOE_SLICES(TT_, RG_)                                                                  \
