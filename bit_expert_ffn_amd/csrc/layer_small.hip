@@ -579,6 +579,13 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
   LS_STAMP(3);
   // ---- C: gate/up + SwiGLU; rows of h (f16) go out with device-scope stores ----
   {
+    // per-XCD mode: the one expert's tensor scales, read before the loop (a load in the item's
+    // epilogue would wait for every weight load in flight)
+    float tsg_x = 0.f, tsu_x = 0.f;
+    if (xm) {
+      tsg_x = a.ts[slot_e[xg] * 3 + 0];
+      tsu_x = a.ts[slot_e[xg] * 3 + 1];
+    }
     float ag[TT], au[TT];
 #pragma unroll
     for (int r = 0; r < TT; ++r) ag[r] = au[r] = 0.f;
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       }
       if (cu.j == nspi - 1) {  // the item's last set: SwiGLU and store two features per lane
         const int e = c_e[ai];
-        const float tsg = a.ts[e * 3 + 0], tsu = a.ts[e * 3 + 1];
+        const float tsg = xm ? tsg_x : a.ts[e * 3 + 0], tsu = xm ? tsu_x : a.ts[e * 3 + 1];
 #pragma unroll
         for (int r = 0; r < TT; ++r) {
           if (r < rows) {
@@ -623,27 +630,41 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
       }
     };
 
-    // two load sets in flight: set s + 1 is requested before set s is used
+    // two load sets in flight: set s + 1 is requested before set s is used.  The loop runs while
+    // two more sets exist and the tail takes the last one or two, so that no set past the end is
+    // requested: its loads would be waited for at the barrier arrival, a full memory latency
     if (nsets > 0) {
       use_set(qgA, quA, sgA, suA, uc);
       cur_next(uc);
-      load_set(qgA, quA, sgA, suA, lc, c_e[lc.ai]);
-      cur_next(lc);
+      if (2 < nsets) {
+        load_set(qgA, quA, sgA, suA, lc, c_e[lc.ai]);
+        cur_next(lc);
+      }
       if (1 < nsets) {
         use_set(qgB, quB, sgB, suB, uc);
         cur_next(uc);
       }
-      for (int s = 2; s < nsets; s += 2) {
+      int s = 2;
+      for (; s + 2 < nsets; s += 2) {  // sets s (in A), s + 1 and s + 2 exist
         load_set(qgB, quB, sgB, suB, lc, c_e[lc.ai]);
         cur_next(lc);
         use_set(qgA, quA, sgA, suA, uc);
         cur_next(uc);
         load_set(qgA, quA, sgA, suA, lc, c_e[lc.ai]);
         cur_next(lc);
-        if (s + 1 < nsets) {
-          use_set(qgB, quB, sgB, suB, uc);
-          cur_next(uc);
-        }
+        use_set(qgB, quB, sgB, suB, uc);
+        cur_next(uc);
+      }
+      if (s + 1 < nsets) {  // the last two sets
+        load_set(qgB, quB, sgB, suB, lc, c_e[lc.ai]);
+        cur_next(lc);
+        use_set(qgA, quA, sgA, suA, uc);
+        cur_next(uc);
+        use_set(qgB, quB, sgB, suB, uc);
+        cur_next(uc);
+      } else if (s < nsets) {  // the last set
+        use_set(qgA, quA, sgA, suA, uc);
+        cur_next(uc);
       }
     }
   }
@@ -732,13 +753,21 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
         racc = 0.f;
       }
     };
-    if (has_k) {
-      for (int s = 0; s < nsets; s += 2) {
+    if (has_k) {  // the loop runs while two more sets exist; the tail requests nothing past the end
+      int s = 0;
+      for (; s + 2 < nsets; s += 2) {
         load_set(qB, sB, s + 1);
         use_set(qA, sA, s);
         if (s == 0) LS_STAMP(12);
         load_set(qA, sA, s + 2);
-        if (s + 1 < nsets) use_set(qB, sB, s + 1);
+        use_set(qB, sB, s + 1);
+      }
+      if (s + 1 < nsets) {
+        load_set(qB, sB, s + 1);
+        use_set(qA, sA, s);
+        use_set(qB, sB, s + 1);
+      } else {
+        use_set(qA, sA, s);
       }
     }
     LS_STAMP(13);
@@ -853,13 +882,21 @@ __global__ __launch_bounds__(256, 2) void layer_small_kernel(LayerSmallArgs a) {
           }
         }
       };
-      if (has_k) {
+      if (has_k) {  // the loop runs while two more sets exist; the tail requests nothing past the end
         if (ftp != (int)blockIdx.x) load_set(qA, sA, 0);
-        for (int s = 0; s < nsets; s += 2) {
+        int s = 0;
+        for (; s + 2 < nsets; s += 2) {
           load_set(qB, sB, s + 1);
           use_set(qA, sA, s);
           load_set(qA, sA, s + 2);
-          if (s + 1 < nsets) use_set(qB, sB, s + 1);
+          use_set(qB, sB, s + 1);
+        }
+        if (s + 1 < nsets) {
+          load_set(qB, sB, s + 1);
+          use_set(qA, sA, s);
+          use_set(qB, sB, s + 1);
+        } else {
+          use_set(qA, sA, s);
         }
       }
       // add the two halves of each feature in LDS, in order
