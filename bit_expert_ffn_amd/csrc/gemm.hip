@@ -251,9 +251,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void ffn_gemm_kernel(
   // pipeline over S register sets.  Set j holds stage s = st + j: its weights feed compute,
   // and right after it the set is refilled with stage s + S; the activations of stage s + 1
   // (loaded S - 1 steps earlier) go to the other LDS buffer, so loads run S - 1 stages ahead.
-  // The main loop covers the largest multiple of S stages with no conditions in its body
-  // (loads past the last stage re-read it, clamped, and are unused); the remaining stages
-  // (fewer than S) follow, each guarded by a uniform condition.
+  // The main loop covers the largest multiple of S stages with no conditions in its body.  With
+  // 32-row tiles (short blocks) its last round skips the refills past the last stage (uniform
+  // conditions): a load left in flight would be waited for before the epilogue reuses its
+  // registers, a memory latency per block.  The host picks S so that the stage count is a
+  // multiple of it where it can: with stages left after that round, the conditional refills
+  // make the compiler wait for every load before each remaining stage.  Larger tiles have long
+  // blocks and re-read the last stage instead (a second copy of the round would make the
+  // 64-row gate/up spill).  The remaining stages (fewer than S) follow, each guarded by a
+  // uniform condition.
   Stage r[S];
   const int last = nstage - 1;
   const int nmain = nstage - nstage % S;
@@ -261,13 +267,35 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void ffn_gemm_kernel(
   for (int jj = 0; jj < S; ++jj) load(r[jj], min(jj, last));
   store_a(r[0], 0);
   lds_barrier();
-  for (int st = 0; st < nmain; st += S) {
+  if constexpr (MT == 32) {
+    int st = 0;
+    for (; st + S < nmain; st += S) {
 #pragma unroll
-    for (int jj = 0; jj < S; ++jj) {
-      compute(r[jj], (st + jj) & 1);
-      store_a(r[(jj + 1) % S], (st + jj + 1) & 1);
-      load(r[jj], min(st + jj + S, last));
-      lds_barrier();
+      for (int jj = 0; jj < S; ++jj) {
+        compute(r[jj], (st + jj) & 1);
+        store_a(r[(jj + 1) % S], (st + jj + 1) & 1);
+        load(r[jj], st + jj + S);
+        lds_barrier();
+      }
+    }
+    if (st < nmain) {
+#pragma unroll
+      for (int jj = 0; jj < S; ++jj) {
+        compute(r[jj], (st + jj) & 1);
+        store_a(r[(jj + 1) % S], (st + jj + 1) & 1);
+        if (st + jj + S < nstage) load(r[jj], st + jj + S);
+        lds_barrier();
+      }
+    }
+  } else {
+    for (int st = 0; st < nmain; st += S) {
+#pragma unroll
+      for (int jj = 0; jj < S; ++jj) {
+        compute(r[jj], (st + jj) & 1);
+        store_a(r[(jj + 1) % S], (st + jj + 1) & 1);
+        load(r[jj], min(st + jj + S, last));
+        lds_barrier();
+      }
     }
   }
 #pragma unroll
@@ -363,7 +391,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
   // 119.3 us)
 #define MOE_GEMM(GU_, MT_, S_, F16_, XBF_, XA_, Q0_, S0_, Q1_, S1_, OUT_)                       \
   do {                                                                                        \
-    constexpr int NW_ = MT_ == 128 ? 8 : (GU_ && MT_ == 32 && S_ == 6) ? 2 : 4;              \
+    constexpr int NW_ = MT_ == 128 ? 8 : (GU_ && MT_ == 32 && S_ >= 6) ? 2 : 4;              \
     const dim3 g_(GU_ ? (a.I + 32 * NW_ - 1) / (32 * NW_) : (a.H + 64 * NW_ - 1) / (64 * NW_), \
                   max_tiles);                                                                 \
     ffn_gemm_kernel<GU_, MT_, F16_, S_, NW_, XBF_><<<g_, 64 * NW_, 0, s>>>(                   \
@@ -379,18 +407,29 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int min_rows, int4* tiles, int32_t*
     else                                                                                      \
       MOE_GEMM(false, MT_, S_, false, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);             \
   } while (0)
-  // register sets of the load pipeline: 4, or 6 for a small batch of narrow experts (I <= 512),
-  // whose few blocks are each bound by the bytes they keep in flight (measured at T = 128,
-  // I = 256: 122 against 132 us; at T = 64, I = 2048, where the blocks fill the chip, 6 sets
-  // cost occupancy: 943 against 921 us)
-  if (MT == 128)
+  // register sets of the load pipeline: 4, or more for the gate/up of a small batch of narrow
+  // experts (I <= 512), whose few blocks are each bound by the bytes they keep in flight
+  // (measured at T = 128, I = 256: 122 against 132 us with 6 sets; at T = 64, I = 2048, where
+  // the blocks fill the chip, 6 sets cost occupancy: 943 against 921 us).  With 32-row tiles the
+  // stage count should be a multiple of the set count (see the kernel's pipeline): the narrow
+  // gate/up takes 8 sets when H / 64 is a multiple of 8 (else 6), its down 4 (K = I: 4 or 8
+  // stages, all requested at once).
+  if (MT == 128) {
     MOE_GEMM_MT(128, kGemmSets, false);
-  else if (MT == 64)
+  } else if (MT == 64) {
     MOE_GEMM_MT(64, kGemmSets, true);
-  else if (a.I <= 512)
-    MOE_GEMM_MT(32, 6, true);
-  else
+  } else if (a.I <= 512) {
+    if ((a.H / gK) % 8 == 0)
+      MOE_GEMM(true, 32, 8, false, true, (const void*)a.x, a.gq, a.gs, a.uq, a.us, a.h16);
+    else
+      MOE_GEMM(true, 32, 6, false, true, (const void*)a.x, a.gq, a.gs, a.uq, a.us, a.h16);
+    if (a.y_f16)
+      MOE_GEMM(false, 32, kGemmSets, true, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+    else
+      MOE_GEMM(false, 32, kGemmSets, false, false, a.h16, a.dq, a.ds, a.dq, a.ds, a.y);
+  } else {
     MOE_GEMM_MT(32, kGemmSets, true);
+  }
 #undef MOE_GEMM_MT
 #undef MOE_GEMM
   return hipGetLastError();
