@@ -251,15 +251,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void ffn_gemm_kernel(
   // pipeline over S register sets.  Set j holds stage s = st + j: its weights feed compute,
   // and right after it the set is refilled with stage s + S; the activations of stage s + 1
   // (loaded S - 1 steps earlier) go to the other LDS buffer, so loads run S - 1 stages ahead.
-  // The main loop covers the largest multiple of S stages with no conditions in its body.  With
-  // 32-row tiles (short blocks) its last round skips the refills past the last stage (uniform
-  // conditions): a load left in flight would be waited for before the epilogue reuses its
-  // registers, a memory latency per block.  The host picks S so that the stage count is a
-  // multiple of it where it can: with stages left after that round, the conditional refills
-  // make the compiler wait for every load before each remaining stage.  Larger tiles have long
-  // blocks and re-read the last stage instead (a second copy of the round would make the
-  // 64-row gate/up spill).  The remaining stages (fewer than S) follow, each guarded by a
-  // uniform condition.
+  // The main loop covers the largest multiple of S stages with no conditions in its body.  Its
+  // last round skips the refills past the last stage (uniform conditions): a load left in
+  // flight would be waited for before the epilogue reuses its registers, a memory latency per
+  // block.  The host picks S so that the stage count is a multiple of it where it can: with
+  // stages left after that round, the conditional refills make the compiler wait for every load
+  // before each remaining stage.  64-row tiles re-read the last stage instead (the second copy
+  // of the round would make their gate/up spill).  The remaining stages (fewer than S) follow,
+  // each guarded by a uniform condition.
   Stage r[S];
   const int last = nstage - 1;
   const int nmain = nstage - nstage % S;
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void ffn_gemm_kernel(
   for (int jj = 0; jj < S; ++jj) load(r[jj], min(jj, last));
   store_a(r[0], 0);
   lds_barrier();
-  if constexpr (MT == 32) {
+  if constexpr (MT != 64) {
     int st = 0;
     for (; st + S < nmain; st += S) {
 #pragma unroll
