@@ -118,11 +118,23 @@ __global__ __launch_bounds__(256) void ffn_gateup_few_kernel(
       }
     }
   };
-  for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
-    load_set(qgB, quB, sgB, suB, c0 + kSet);
-    use_set(qgA, quA, sgA, suA, c0);
-    load_set(qgA, quA, sgA, suA, c0 + 2 * kSet);
-    use_set(qgB, quB, sgB, suB, c0 + kSet);
+  // sets of kSet chunks: the loop runs while two more sets exist and the tail takes the last one
+  // or two, so no set past the end is requested (its loads would be waited for at the block's
+  // reduction, a memory latency)
+  const int nsets = (nchunk + kSet - 1) / kSet;
+  int s = 0;
+  for (; s + 2 < nsets; s += 2) {
+    load_set(qgB, quB, sgB, suB, (s + 1) * kSet);
+    use_set(qgA, quA, sgA, suA, s * kSet);
+    load_set(qgA, quA, sgA, suA, (s + 2) * kSet);
+    use_set(qgB, quB, sgB, suB, (s + 1) * kSet);
+  }
+  if (s + 1 < nsets) {
+    load_set(qgB, quB, sgB, suB, (s + 1) * kSet);
+    use_set(qgA, quA, sgA, suA, s * kSet);
+    use_set(qgB, quB, sgB, suB, (s + 1) * kSet);
+  } else {
+    use_set(qgA, quA, sgA, suA, s * kSet);
   }
   // K-groups of a feature (cross-lane), then the block's K slices in order (LDS)
 #pragma unroll
@@ -225,11 +237,21 @@ __global__ __launch_bounds__(256) void ffn_down_few_kernel(
       }
     }
   };
-  for (int c0 = 0; c0 < nchunk; c0 += 2 * kSet) {
-    load_set(qB, sB, c0 + kSet);
-    use_set(qA, sA, c0);
-    load_set(qA, sA, c0 + 2 * kSet);
-    use_set(qB, sB, c0 + kSet);
+  // the loop runs while two more sets exist; the tail requests nothing past the end
+  const int nsets = (nchunk + kSet - 1) / kSet;
+  int s = 0;
+  for (; s + 2 < nsets; s += 2) {
+    load_set(qB, sB, (s + 1) * kSet);
+    use_set(qA, sA, s * kSet);
+    load_set(qA, sA, (s + 2) * kSet);
+    use_set(qB, sB, (s + 1) * kSet);
+  }
+  if (s + 1 < nsets) {
+    load_set(qB, sB, (s + 1) * kSet);
+    use_set(qA, sA, s * kSet);
+    use_set(qB, sB, (s + 1) * kSet);
+  } else {
+    use_set(qA, sA, s * kSet);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
