@@ -344,6 +344,7 @@ __global__ __launch_bounds__(256 * P) void router_select_kernel(
     int k, float* __restrict__ logits, int32_t* __restrict__ topk_id,
     float* __restrict__ topk_w) {
   __shared__ __attribute__((aligned(16))) uint64_t key[kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint64_t cand[4 * 32];  // two-level selection (k <= 32)
   __shared__ float lv[kMaxExperts];
   __shared__ int rank[kMaxExperts];
   __shared__ float selv[kMaxExperts];
@@ -383,17 +384,45 @@ __global__ __launch_bounds__(256 * P) void router_select_kernel(
     }
   }
   __syncthreads();
-  // rank: thread (e, q) counts the larger keys among 256/P of them
-  if (e < E) {
-    const uint64_t ke = key[e];
+  if (P == 1 && k <= 32) {
+    // two levels: each expert is ranked among the 64 keys of its wavefront; those of rank < k
+    // are the candidates (the overall top k are among them), which are then ranked among each
+    // other.  rank[e] is the overall rank for the top k and at least k for the others.
+    const int wv = tid >> 6, lane = tid & 63;
+    const uint64_t ke = key[tid];
+    if (tid < 4 * k) cand[tid] = 0;
     int r = 0;
-    constexpr int span = kMaxExperts / P;
+    const uint4* kp = reinterpret_cast<const uint4*>(key + wv * 64);
 #pragma unroll 8
-    for (int j = q * span; j < q * span + span; ++j) r += key[j] > ke;
-    if (P > 1)
-      atomicAdd(&rank[e], r);
-    else
-      rank[e] = r;
+    for (int j = 0; j < 32; ++j) {
+      const uint4 v = kp[j];
+      r += (((uint64_t)v.y << 32) | v.x) > ke;
+      r += (((uint64_t)v.w << 32) | v.z) > ke;
+    }
+    __syncthreads();
+    if (ke != 0 && r < k) cand[wv * k + r] = ke;
+    if (e < E) rank[e] = k;
+    __syncthreads();
+    if (tid < 4 * k) {
+      const uint64_t kc = cand[tid];
+      int rc = 0;
+      for (int j = 0; j < 4 * k; ++j) rc += cand[j] > kc;
+      if (kc != 0 && rc < k) rank[kMaxExperts - 1 - (int)(uint32_t)kc] = rc;
+    }
+    (void)lane;
+  } else {
+    // rank: thread (e, q) counts the larger keys among 256/P of them
+    if (e < E) {
+      const uint64_t ke = key[e];
+      int r = 0;
+      constexpr int span = kMaxExperts / P;
+#pragma unroll 8
+      for (int j = q * span; j < q * span + span; ++j) r += key[j] > ke;
+      if (P > 1)
+        atomicAdd(&rank[e], r);
+      else
+        rank[e] = r;
+    }
   }
   __syncthreads();
   if (q == 0 && e < E && rank[e] < k) selv[rank[e]] = lv[e];
