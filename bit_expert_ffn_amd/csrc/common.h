@@ -15,8 +15,9 @@ namespace moe {
 constexpr int kMaxExperts = 256;
 // rows handled by the one-block grouping kernel; above this the three-pass grouping runs
 constexpr int kGroupSmallMax = 16384;
-// slots per block of the three-pass grouping (16 waves x 1024 slots)
-constexpr int kGroupChunk = 16384;
+// slots per block of the three-pass grouping (16 waves x 256 slots: at 131,072 slots, 32 blocks
+// for the histogram and scatter passes)
+constexpr int kGroupChunk = 4096;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

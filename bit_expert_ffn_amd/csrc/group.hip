@@ -141,36 +141,62 @@ __global__ __launch_bounds__(1024) void group_hist_kernel(const int32_t* __restr
   }
 }
 
-// Pass 2 (one block): per-expert exclusive scan over all wavefronts, offsets, active list.
-// whist entries become each wavefront's first row for the expert.
-__global__ __launch_bounds__(256) void group_scan_kernel(int32_t* __restrict__ whist, int nw,
-                                                         int E, int32_t* __restrict__ count,
-                                                         int32_t* __restrict__ offset,
-                                                         int32_t* __restrict__ active,
-                                                         int32_t* __restrict__ n_active) {
+// Pass 2 (one block of 1024 threads): per-expert exclusive scan over all wavefronts, offsets,
+// active list.  Thread (q, e) takes quarter q of the wavefront range of expert e, with up to 64
+// loads in flight: first its quarter's total, then (after the offsets) each wavefront's first
+// row.  whist entries become each wavefront's first row for the expert.
+__global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ whist, int nw,
+                                                          int E, int32_t* __restrict__ count,
+                                                          int32_t* __restrict__ offset,
+                                                          int32_t* __restrict__ active,
+                                                          int32_t* __restrict__ n_active) {
+  constexpr int kB = 64;  // loads in flight per thread
   __shared__ __attribute__((aligned(16))) int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
+  __shared__ int part[4][kMaxExperts];
   const int tid = threadIdx.x;
-  cnt[tid] = 0;  // 256 threads
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-#pragma unroll 8
-    for (int w = 0; w < nw; ++w) {
-      const int c = whist[(size_t)w * E + tid];
-      whist[(size_t)w * E + tid] = run;
-      run += c;
+  // q is the same for the four wavefronts of a quarter: made uniform, the row offsets below are
+  // scalar and each load takes one scalar base plus the lane's expert offset
+  const int e = tid & (kMaxExperts - 1), q = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int per = (nw + 3) / 4, w0 = min(nw, q * per), w1 = min(nw, w0 + per);
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  int tot = 0;
+  if (e < E) {
+    for (int wb = w0; wb < w1; wb += kB) {
+      // unconditional loads (past w1 clamped, not added), so that all of them are in flight
+      int c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = (whist + (size_t)min(wb + u, w1 - 1) * E)[e];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) tot += wb + u < w1 ? c[u] : 0;
     }
-    cnt[tid] = run;
   }
+  part[q][e] = tot;
+  __syncthreads();
+  if (tid < E) cnt[tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
   __syncthreads();
   if (tid < 64) wave_scan_offsets(cnt, E, off);
   __syncthreads();
+  if (e < E) {
+    int run = off[e];
+    for (int j = 0; j < q; ++j) run += part[j][e];
+    for (int wb = w0; wb < w1; wb += kB) {
+      int c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = (whist + (size_t)min(wb + u, w1 - 1) * E)[e];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (wb + u < w1) {
+          (whist + (size_t)(wb + u) * E)[e] = run;
+          run += c[u];
+        }
+      }
+    }
+  }
   if (tid < E) {
     count[tid] = cnt[tid];
     offset[tid] = off[tid];
     if (tid == 0) offset[E] = off[E];
-    for (int w = 0; w < nw; ++w) whist[(size_t)w * E + tid] += off[tid];
   }
   place_active(cnt, E, active, n_active);
 }
@@ -207,8 +233,8 @@ hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* count,
     if (plan && plan->MT > 0) return hipErrorInvalidValue;  // the three-pass grouping plans nothing
     const int nblk = (n + kGroupChunk - 1) / kGroupChunk;
     group_hist_kernel<<<nblk, 1024, 0, s>>>(ids, n, E, whist);
-    group_scan_kernel<<<1, 256, 0, s>>>(whist, nblk * kGroupWaves, E, count, offset, active,
-                                        n_active);
+    group_scan_kernel<<<1, 1024, 0, s>>>(whist, nblk * kGroupWaves, E, count, offset, active,
+                                         n_active);
     group_scatter_kernel<<<nblk, 1024, 0, s>>>(ids, n, E, whist, sorted_slot, slot_row);
   }
   return hipGetLastError();
